@@ -1,0 +1,157 @@
+"""ctypes front end of the fp64 verify-attention oracle (oracle.c).
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import this package.  It shares no code with the HIP
+library and never calls it.
+
+The functions accept any object that carries the workload attributes
+(num_seqs, B, H, KVH, D, num_pages, max_pages, q_dtype, kv_dtype, scale, q,
+k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent) with the
+layouts documented in oracle.h.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_DT = {"f32": 0, "f16": 1, "bf16": 2, "q8_0": 3}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (portable x86-64, -O2)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+                               "-o", tmp, _SRC, "-lpthread", "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("num_seqs", "B", "H", "KVH", "D", "num_pages", "max_pages", "q_dtype", "kv_dtype")] + [
+        ("scale", ctypes.c_double)]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, dp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        sp = ctypes.POINTER(_Shape)
+        lib.orc_attention.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, dp, dp, ctypes.c_int]
+        lib.orc_attention_items.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ctypes.c_int32, ip, dp, dp,
+                                            ctypes.c_int]
+        lib.orc_split_partials.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ctypes.c_int32, ip, dp, dp, dp,
+                                           ctypes.c_int]
+        lib.orc_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, dp, dp, dp, dp, dp]
+        for f in (lib.orc_attention, lib.orc_attention_items, lib.orc_split_partials, lib.orc_merge):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+class OracleError(ValueError):
+    pass
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _prep(w):
+    shape = _Shape(num_seqs=w.num_seqs, B=w.B, H=w.H, KVH=w.KVH, D=w.D, num_pages=w.num_pages,
+                   max_pages=w.max_pages, q_dtype=_DT[w.q_dtype], kv_dtype=_DT[w.kv_dtype],
+                   scale=float(np.float32(w.scale)))
+    arrs = dict(
+        q=np.ascontiguousarray(w.q), k=np.ascontiguousarray(w.k_pool), v=np.ascontiguousarray(w.v_pool),
+        ks=None if w.k_scale is None else np.ascontiguousarray(w.k_scale).view(np.uint16),
+        vs=None if w.v_scale is None else np.ascontiguousarray(w.v_scale).view(np.uint16),
+        bt=np.ascontiguousarray(w.block_table, dtype=np.int32),
+        ctx=np.ascontiguousarray(w.ctx_lens, dtype=np.int32),
+        par=None if w.parent is None else np.ascontiguousarray(w.parent, dtype=np.int32),
+    )
+    if w.q_dtype in ("f16", "bf16"):
+        arrs["q"] = arrs["q"].view(np.uint16)
+    return shape, arrs
+
+
+def _common(a):
+    return (_ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["ks"]), _ptr(a["vs"]), _ptr(a["bt"]),
+            _ptr(a["ctx"]), _ptr(a["par"]))
+
+
+def default_threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def attention(w, nthreads: Optional[int] = None):
+    """Definition evaluated in fp64 -> (out [nseq*B, H, D], lse [nseq*B, H])."""
+    lib = _load()
+    shape, a = _prep(w)
+    out = np.zeros((w.num_seqs * w.B, w.H, w.D), np.float64)
+    lse = np.zeros((w.num_seqs * w.B, w.H), np.float64)
+    rc = lib.orc_attention(ctypes.byref(shape), *_common(a), _ptr(out), _ptr(lse),
+                           nthreads or default_threads())
+    if rc != 0:
+        raise OracleError("oracle rejected the inputs (rc=%d)" % rc)
+    return out, lse
+
+
+def attention_items(w, items: Sequence[Sequence[int]], nthreads: Optional[int] = None):
+    """Definition for chosen (seq, row, head) triples -> (out [n, D], lse [n])."""
+    lib = _load()
+    shape, a = _prep(w)
+    it = np.ascontiguousarray(np.asarray(items, np.int32).reshape(-1, 3))
+    out = np.zeros((it.shape[0], w.D), np.float64)
+    lse = np.zeros((it.shape[0],), np.float64)
+    rc = lib.orc_attention_items(ctypes.byref(shape), *_common(a), it.shape[0], _ptr(it), _ptr(out), _ptr(lse),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise OracleError("oracle rejected the inputs (rc=%d)" % rc)
+    return out, lse
+
+
+def split_partials(w, bounds: np.ndarray, nthreads: Optional[int] = None):
+    """Split partials for a token partition bounds [nseq, S+1] -> (m, l, o)."""
+    lib = _load()
+    shape, a = _prep(w)
+    b = np.ascontiguousarray(bounds, np.int32)
+    S = b.shape[1] - 1
+    nrows = w.num_seqs * w.B * w.H
+    m = np.zeros((S, nrows), np.float64)
+    l = np.zeros((S, nrows), np.float64)
+    o = np.zeros((S, nrows, w.D), np.float64)
+    rc = lib.orc_split_partials(ctypes.byref(shape), *_common(a), S, _ptr(b), _ptr(m), _ptr(l), _ptr(o),
+                                nthreads or default_threads())
+    if rc != 0:
+        raise OracleError("oracle rejected the inputs (rc=%d)" % rc)
+    return m, l, o
+
+
+def merge(m: np.ndarray, l: np.ndarray, o: np.ndarray):
+    """Log-sum-exp merge of split partials -> (out [nrows, D], lse [nrows])."""
+    lib = _load()
+    m = np.ascontiguousarray(m, np.float64)
+    l = np.ascontiguousarray(l, np.float64)
+    o = np.ascontiguousarray(o, np.float64)
+    S, nrows = m.shape
+    D = o.shape[-1]
+    out = np.zeros((nrows, D), np.float64)
+    lse = np.zeros((nrows,), np.float64)
+    rc = lib.orc_merge(S, nrows, D, _ptr(m), _ptr(l), _ptr(o), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise OracleError("merge rejected the inputs (rc=%d)" % rc)
+    return out, lse

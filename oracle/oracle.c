@@ -1,0 +1,408 @@
+/*
+ * fp64 CPU oracle for speculative-decoding verify attention.
+ *
+ * TEST INFRASTRUCTURE (see oracle.h): only tests/, __graft_entry__.smoke() and
+ * bench.py's cpu_baseline leg use it.  Plain loops in the order the definition
+ * states them; the only parallelism is a pthread split over independent
+ * (row, head) outputs so it can be timed on many cores.  No blocking, no
+ * fusion, no reordering of any sum.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_PAGE 16
+
+/* ---- scalar decoders (IEEE binary16 / bfloat16 bit patterns -> double) ---- */
+
+static double f16_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(m + 1024), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+static double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double load_q(const orc_shape* p, const void* q, int64_t idx) {
+  switch (p->q_dtype) {
+    case ORC_F32: return (double)((const float*)q)[idx];
+    case ORC_F16: return f16_to_double(((const uint16_t*)q)[idx]);
+    default: return bf16_to_double(((const uint16_t*)q)[idx]);
+  }
+}
+
+/* ---- validation ---- */
+
+static int check_shape(const orc_shape* p) {
+  if (p->num_seqs < 1 || p->B < 1 || p->H < 1 || p->KVH < 1 || p->D < 1) return ORC_EINVAL;
+  if (p->H % p->KVH) return ORC_EINVAL;
+  if (p->kv_dtype == ORC_Q8 && p->D % 32) return ORC_EINVAL;
+  if (p->q_dtype != ORC_F32 && p->q_dtype != ORC_F16 && p->q_dtype != ORC_BF16) return ORC_EINVAL;
+  if (p->kv_dtype != ORC_F32 && p->kv_dtype != ORC_F16 && p->kv_dtype != ORC_Q8) return ORC_EINVAL;
+  return ORC_OK;
+}
+
+static int check_seq(const orc_shape* p, const int32_t* bt, const int32_t* ctx_lens,
+                     const int32_t* parent, int s) {
+  int ctx = ctx_lens[s];
+  if (ctx < p->B || ctx > p->max_pages * ORC_PAGE) return ORC_EINVAL;
+  for (int pg = 0; pg < (ctx + ORC_PAGE - 1) / ORC_PAGE; ++pg) {
+    int id = bt[(int64_t)s * p->max_pages + pg];
+    if (id < 0 || id >= p->num_pages) return ORC_EINVAL;
+  }
+  if (parent) {
+    for (int i = 0; i < p->B; ++i) {
+      int par = parent[(int64_t)s * p->B + i];
+      if (par < -1 || par >= i) return ORC_EINVAL;
+    }
+  }
+  return ORC_OK;
+}
+
+/* anc[i*B + a] = 1 iff in-window row a is row i or one of its ancestors. */
+static void build_ancestry(const int32_t* par_s, int B, unsigned char* anc) {
+  memset(anc, 0, (size_t)B * B);
+  for (int i = 0; i < B; ++i) {
+    int a = i;
+    while (a >= 0) {
+      anc[i * B + a] = 1;
+      a = par_s ? par_s[a] : a - 1;
+    }
+  }
+}
+
+/* ---- K / V gather and decode for one (sequence, KV head) ---- */
+
+static void decode_seq_kv(const orc_shape* p, const void* k_pool, const void* v_pool,
+                          const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* bt,
+                          int s, int g, int ctx, double* K, double* V) {
+  const int D = p->D, KVH = p->KVH;
+  for (int j = 0; j < ctx; ++j) {
+    int64_t page = bt[(int64_t)s * p->max_pages + j / ORC_PAGE];
+    int slot = j % ORC_PAGE;
+    int64_t krow = ((page * KVH + g) * ORC_PAGE + slot) * D;   /* k_pool[page][g][slot][:] */
+    int64_t vbase = (page * KVH + g) * (int64_t)D * ORC_PAGE;  /* v_pool[page][g][:][:]    */
+    for (int d = 0; d < D; ++d) {
+      int64_t vidx = vbase + (int64_t)d * ORC_PAGE + slot;     /* v_pool[page][g][d][slot] */
+      double kx, vx;
+      if (p->kv_dtype == ORC_Q8) {
+        int8_t kq = ((const int8_t*)k_pool)[krow + d];
+        int8_t vq = ((const int8_t*)v_pool)[vidx];
+        /* k_scale[page][g][slot][d/32], v_scale[page][g][d/32][slot] */
+        double kd = f16_to_double(k_scale[((page * KVH + g) * ORC_PAGE + slot) * (D / 32) + d / 32]);
+        double vd = f16_to_double(v_scale[((page * KVH + g) * (D / 32) + d / 32) * ORC_PAGE + slot]);
+        kx = kd * (double)kq;
+        vx = vd * (double)vq;
+      } else if (p->kv_dtype == ORC_F16) {
+        kx = f16_to_double(((const uint16_t*)k_pool)[krow + d]);
+        vx = f16_to_double(((const uint16_t*)v_pool)[vidx]);
+      } else {
+        kx = (double)((const float*)k_pool)[krow + d];
+        vx = (double)((const float*)v_pool)[vidx];
+      }
+      K[(int64_t)j * D + d] = kx;
+      V[(int64_t)j * D + d] = vx;
+    }
+  }
+}
+
+/* ---- one (row, head): definition or one split of the split form ---- */
+
+typedef struct {
+  const orc_shape* p;
+  const void* q;
+  const double* K;
+  const double* V;
+  const unsigned char* anc;
+  int s, ctx;
+} seq_ctx;
+
+static int visible(const seq_ctx* c, int i, int j) {
+  int base = c->ctx - c->p->B;
+  if (j < base) return 1;
+  return c->anc[i * c->p->B + (j - base)];
+}
+
+static double score(const seq_ctx* c, int i, int h, int j) {
+  const orc_shape* p = c->p;
+  int64_t qrow = ((int64_t)(c->s * p->B + i) * p->H + h) * p->D;
+  double acc = 0.0;
+  for (int d = 0; d < p->D; ++d) acc += load_q(p, c->q, qrow + d) * c->K[(int64_t)j * p->D + d];
+  return p->scale * acc;
+}
+
+/* Definition: O and lse over all of Vis(i). */
+static void attend_direct(const seq_ctx* c, int i, int h, double* z, double* o, double* lse) {
+  const int D = c->p->D;
+  double M = -INFINITY;
+  for (int j = 0; j < c->ctx; ++j) {
+    if (!visible(c, i, j)) continue;
+    z[j] = score(c, i, h, j);
+    if (z[j] > M) M = z[j];
+  }
+  double L = 0.0;
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  for (int j = 0; j < c->ctx; ++j) {
+    if (!visible(c, i, j)) continue;
+    double w = exp(z[j] - M);
+    L += w;
+    for (int d = 0; d < D; ++d) o[d] += w * c->V[(int64_t)j * D + d];
+  }
+  for (int d = 0; d < D; ++d) o[d] /= L;
+  *lse = M + log(L);
+}
+
+/* One split [lo, hi): unnormalised (m, l, O). */
+static void attend_split(const seq_ctx* c, int i, int h, int lo, int hi, double* z, double* m,
+                         double* l, double* o) {
+  const int D = c->p->D;
+  double mk = -INFINITY;
+  for (int j = lo; j < hi; ++j) {
+    if (!visible(c, i, j)) continue;
+    z[j] = score(c, i, h, j);
+    if (z[j] > mk) mk = z[j];
+  }
+  double lk = 0.0;
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  if (mk != -INFINITY) {
+    for (int j = lo; j < hi; ++j) {
+      if (!visible(c, i, j)) continue;
+      double w = exp(z[j] - mk);
+      lk += w;
+      for (int d = 0; d < D; ++d) o[d] += w * c->V[(int64_t)j * D + d];
+    }
+  }
+  *m = mk;
+  *l = lk;
+}
+
+/* ---- threading over (row, head) work items of one sequence / KV head ---- */
+
+typedef struct {
+  const seq_ctx* c;
+  int mode; /* 0 direct into full arrays, 1 split partials, 2 direct into item arrays */
+  int g, G;
+  int n_work;
+  const int32_t* work; /* pairs (i, h) */
+  const int32_t* item_index; /* mode 2: destination index per work item */
+  int tid, nthreads;
+  /* outputs */
+  double* out;
+  double* lse;
+  int nsplit;
+  const int32_t* bounds;
+  double* m;
+  double* l;
+  double* o;
+  int64_t nrows_total;
+} job;
+
+static void* run_job(void* arg) {
+  job* jb = (job*)arg;
+  const seq_ctx* c = jb->c;
+  const orc_shape* p = c->p;
+  double* z = (double*)malloc(sizeof(double) * (size_t)(c->ctx > 0 ? c->ctx : 1));
+  for (int w = jb->tid; w < jb->n_work; w += jb->nthreads) {
+    int i = jb->work[2 * w], h = jb->work[2 * w + 1];
+    int64_t row = (int64_t)(c->s * p->B + i) * p->H + h; /* (seq*B + i, h) */
+    if (jb->mode == 0) {
+      attend_direct(c, i, h, z, jb->out + row * p->D, jb->lse + row);
+    } else if (jb->mode == 2) {
+      int64_t dst = jb->item_index[w];
+      attend_direct(c, i, h, z, jb->out + dst * p->D, jb->lse + dst);
+    } else {
+      const int32_t* b = jb->bounds + (int64_t)c->s * (jb->nsplit + 1);
+      for (int k = 0; k < jb->nsplit; ++k) {
+        int64_t r = (int64_t)k * jb->nrows_total + row;
+        attend_split(c, i, h, b[k], b[k + 1], z, jb->m + r, jb->l + r, jb->o + r * p->D);
+      }
+    }
+  }
+  free(z);
+  return NULL;
+}
+
+static void run_parallel(job* proto, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  job jobs[256];
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = *proto;
+    jobs[t].tid = t;
+    jobs[t].nthreads = nthreads;
+  }
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&th[t], NULL, run_job, &jobs[t]) != 0) break;
+    started = t;
+  }
+  run_job(&jobs[0]);
+  for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+  /* any thread that failed to start: run its share here */
+  for (int t = started + 1; t < nthreads; ++t) run_job(&jobs[t]);
+}
+
+/* Shared driver: for every sequence and KV head, decode K/V, then evaluate the
+ * requested (row, head) items. */
+static int drive(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
+                 const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* bt,
+                 const int32_t* ctx_lens, const int32_t* parent, int mode, int32_t n_items,
+                 const int32_t* items, double* out, double* lse, int32_t nsplit,
+                 const int32_t* bounds, double* m, double* l, double* o, int nthreads) {
+  if (check_shape(p) != ORC_OK) return ORC_EINVAL;
+  if (p->kv_dtype == ORC_Q8 && (!k_scale || !v_scale)) return ORC_EINVAL;
+  for (int s = 0; s < p->num_seqs; ++s)
+    if (check_seq(p, bt, ctx_lens, parent, s) != ORC_OK) return ORC_EINVAL;
+  if (mode == 1) {
+    if (nsplit < 1) return ORC_EINVAL;
+    for (int s = 0; s < p->num_seqs; ++s) {
+      const int32_t* b = bounds + (int64_t)s * (nsplit + 1);
+      if (b[0] != 0 || b[nsplit] != ctx_lens[s]) return ORC_EINVAL;
+      for (int k = 0; k < nsplit; ++k)
+        if (b[k + 1] < b[k]) return ORC_EINVAL;
+    }
+  }
+  if (mode == 2) {
+    for (int t = 0; t < n_items; ++t) {
+      int s = items[3 * t], i = items[3 * t + 1], h = items[3 * t + 2];
+      if (s < 0 || s >= p->num_seqs || i < 0 || i >= p->B || h < 0 || h >= p->H) return ORC_EINVAL;
+    }
+  }
+
+  const int G = p->H / p->KVH;
+  const int64_t nrows_total = (int64_t)p->num_seqs * p->B * p->H;
+  unsigned char* anc = (unsigned char*)malloc((size_t)p->B * p->B);
+  int32_t* work = (int32_t*)malloc(sizeof(int32_t) * 2 * (size_t)(p->B * G > n_items ? p->B * G : n_items + 1));
+  int32_t* widx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_items + 1));
+  if (!anc || !work || !widx) {
+    free(anc); free(work); free(widx);
+    return ORC_EINVAL;
+  }
+  int rc = ORC_OK;
+  for (int s = 0; s < p->num_seqs && rc == ORC_OK; ++s) {
+    int ctx = ctx_lens[s];
+    build_ancestry(parent ? parent + (int64_t)s * p->B : NULL, p->B, anc);
+    for (int g = 0; g < p->KVH; ++g) {
+      int n_work = 0;
+      if (mode == 2) {
+        for (int t = 0; t < n_items; ++t) {
+          if (items[3 * t] != s || items[3 * t + 2] / G != g) continue;
+          work[2 * n_work] = items[3 * t + 1];
+          work[2 * n_work + 1] = items[3 * t + 2];
+          widx[n_work] = t;
+          ++n_work;
+        }
+      } else {
+        for (int hh = 0; hh < G; ++hh)
+          for (int i = 0; i < p->B; ++i) {
+            work[2 * n_work] = i;
+            work[2 * n_work + 1] = g * G + hh;
+            ++n_work;
+          }
+      }
+      if (n_work == 0) continue;
+      double* K = (double*)malloc(sizeof(double) * (size_t)ctx * p->D);
+      double* V = (double*)malloc(sizeof(double) * (size_t)ctx * p->D);
+      if (!K || !V) {
+        free(K); free(V);
+        rc = ORC_EINVAL;
+        break;
+      }
+      decode_seq_kv(p, k_pool, v_pool, k_scale, v_scale, bt, s, g, ctx, K, V);
+      seq_ctx c = {p, q, K, V, anc, s, ctx};
+      job proto;
+      memset(&proto, 0, sizeof proto);
+      proto.c = &c;
+      proto.mode = mode;
+      proto.g = g;
+      proto.G = G;
+      proto.n_work = n_work;
+      proto.work = work;
+      proto.item_index = widx;
+      proto.out = out;
+      proto.lse = lse;
+      proto.nsplit = nsplit;
+      proto.bounds = bounds;
+      proto.m = m;
+      proto.l = l;
+      proto.o = o;
+      proto.nrows_total = nrows_total;
+      run_parallel(&proto, nthreads);
+      free(K);
+      free(V);
+    }
+  }
+  free(anc);
+  free(work);
+  free(widx);
+  return rc;
+}
+
+int orc_attention(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
+                  const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
+                  const int32_t* ctx_lens, const int32_t* parent, double* out, double* lse,
+                  int nthreads) {
+  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, 0, 0, NULL,
+               out, lse, 0, NULL, NULL, NULL, NULL, nthreads);
+}
+
+int orc_attention_items(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
+                        const uint16_t* k_scale, const uint16_t* v_scale,
+                        const int32_t* block_table, const int32_t* ctx_lens,
+                        const int32_t* parent, int32_t n_items, const int32_t* items,
+                        double* out, double* lse, int nthreads) {
+  if (n_items < 0 || (n_items > 0 && !items)) return ORC_EINVAL;
+  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, 2, n_items,
+               items, out, lse, 0, NULL, NULL, NULL, NULL, nthreads);
+}
+
+int orc_split_partials(const orc_shape* p, const void* q, const void* k_pool,
+                       const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
+                       const int32_t* block_table, const int32_t* ctx_lens,
+                       const int32_t* parent, int32_t nsplit, const int32_t* bounds, double* m,
+                       double* l, double* o, int nthreads) {
+  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, 1, 0, NULL,
+               NULL, NULL, nsplit, bounds, m, l, o, nthreads);
+}
+
+int orc_merge(int32_t nsplit, int64_t nrows, int32_t D, const double* m, const double* l,
+              const double* o, double* out, double* lse) {
+  if (nsplit < 1 || nrows < 0 || D < 1) return ORC_EINVAL;
+  for (int64_t r = 0; r < nrows; ++r) {
+    double M = -INFINITY;
+    for (int k = 0; k < nsplit; ++k) {
+      int64_t e = (int64_t)k * nrows + r;
+      if (l[e] > 0.0 && m[e] > M) M = m[e];
+    }
+    double L = 0.0;
+    for (int d = 0; d < D; ++d) out[r * D + d] = 0.0;
+    for (int k = 0; k < nsplit; ++k) {
+      int64_t e = (int64_t)k * nrows + r;
+      if (!(l[e] > 0.0)) continue; /* empty split */
+      double w = exp(m[e] - M);
+      L += w * l[e];
+      for (int d = 0; d < D; ++d) out[r * D + d] += w * o[e * D + d];
+    }
+    for (int d = 0; d < D; ++d) out[r * D + d] /= L;
+    lse[r] = M + log(L);
+  }
+  return ORC_OK;
+}
