@@ -1,0 +1,196 @@
+/*
+ * verify_attn.h -- C ABI of the MI355X (gfx950) speculative-decoding verify
+ * attention library (libverify_attn.so).
+ *
+ * WHAT IT COMPUTES
+ *   B drafted query rows per sequence attend over that sequence's paged KV
+ *   cache with a causal or draft-tree mask, grouped-query heads, and fp16 or
+ *   8-bit KV, evaluated as a split-KV (flash-decoding) schedule: one partial
+ *   kernel writes per-split (running max m, sum l, unnormalised O) and a
+ *   log-sum-exp merge kernel combines them.  Sources:
+ *     - page "perf(gfx1100): speed up long-context DFlash verify 13.4% with FA2
+ *       split-KV and retain HipGraph/Redline PM4": Summary (split-KV S8 for
+ *       B=16 verify, caller-owned partial workspace); Default and admission
+ *       policy (dense H24/KV4/D256, B 4..32, fail-closed admission); Performance,
+ *       batch-16 kernel screen (separate partial / merge / direct entries, S1 is
+ *       the direct path);
+ *     - page "perf(gfx11): optimize Qwen DFlash speculative verify": alpineQ's
+ *       notes (one KV fetch shared by many query rows, q8_0 KV);
+ *     - page "perf(qwen35): retain speculation during paged prefill": Mechanism
+ *       and State and commit invariants (tree rows use ancestry metadata over
+ *       the fixed suffix; other rows are positioned causal reads), Correctness
+ *       failure found during qualification (16-token paged blocks; direct rows
+ *       must not change when other rows join the launch).
+ *
+ *   For sequence s (ctx = ctx_lens[s] valid tokens, the B drafted rows
+ *   included), drafted row i (0 <= i < B) sits at token slot base + i with
+ *   base = ctx - B.  Its ancestor set anc(i) = {i} + anc(parent[i]) when
+ *   parent[i] >= 0 (parent == NULL means parent[i] = i - 1, i.e. causal).  Row
+ *   i sees tokens [0, base) plus {base + a : a in anc(i)}.  Query head h reads
+ *   KV head h / (H / KVH).  out = softmax(scale * q k^T) v over the visible
+ *   tokens; lse = natural log of the softmax denominator (with the max folded
+ *   back in).
+ *
+ * MEMORY LAYOUTS (all C-contiguous, device memory unless marked host)
+ *   q           [num_seqs*B, H, D]            q_dtype (F32 | F16 | BF16)
+ *   k_pool      [num_pages, KVH, 16, D]       token-major: one D-vector per slot
+ *   v_pool      [num_pages, KVH, D, 16]       dim-major: the 16 slots of a page
+ *                                             are contiguous for each dimension
+ *   k_scale     [num_pages, KVH, 16, D/32]    f16, Q8_0 only (else NULL)
+ *   v_scale     [num_pages, KVH, D/32, 16]    f16, Q8_0 only (else NULL)
+ *   block_table [num_seqs, max_pages_per_seq] int32 physical page ids
+ *   ctx_lens    [num_seqs]                    int32
+ *   parent      [num_seqs, B]                 int32, or NULL for causal
+ *   out         [num_seqs*B, H, D]            out_dtype (F16 | BF16 | F32)
+ *   lse         [num_seqs*B, H]               f32, optional (NULL = not written)
+ *   Q8_0: each KV element is int8 q with value scale * q, one f16 scale per
+ *   32 consecutive head_dim indices of one (token, KV head).  Token j of
+ *   sequence s lives in page block_table[s][j / 16], slot j % 16.
+ *   The V page is stored dim-major because the P.V contraction reduces over
+ *   tokens: that way a matrix-core operand (8 consecutive tokens of one
+ *   dimension) is one contiguous load.
+ *
+ * OWNERSHIP AND STREAMS
+ *   The caller owns every device buffer and the stream.  The library never
+ *   allocates device memory, never synchronises inside verify_attn_run, and
+ *   enqueues its kernels asynchronously on `stream` (a hipStream_t; NULL is the
+ *   null stream).  A plan is immutable host memory owned by the library until
+ *   verify_attn_plan_destroy; it may be shared across threads and streams.
+ *   Concurrent runs need distinct workspaces.
+ *
+ * WORKSPACE
+ *   verify_attn_plan reports workspace_bytes.  The first 256 bytes hold a
+ *   uint32 flag word (kernels OR error bits into it); the rest holds the fp32
+ *   split partials.  Zero the workspace once after allocating it; the flags
+ *   stay set until verify_attn_read_flags clears them.
+ *
+ * ERRORS (fail closed: nothing is launched on any error)
+ *   VA_EUNSUPPORTED  shape or dtype outside what the kernels implement
+ *   VA_EINVAL        NULL or misaligned (16 B) required pointer, bad argument
+ *   VA_EWORKSPACE    workspace smaller than the plan needs, or num_splits
+ *                    above the plan's maximum
+ *   VA_EHIP          a HIP call or kernel launch failed
+ *   Device-resident metadata (ctx_lens, block_table, parent) is validated on
+ *   the device: a bad value sets a bit in the flag word (VA_FLAG_*) and the
+ *   affected sequence's outputs become NaN; no out-of-range memory is read.
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VA_OK = 0,
+  VA_EINVAL = -1,
+  VA_EUNSUPPORTED = -2,
+  VA_EWORKSPACE = -3,
+  VA_EHIP = -4
+} va_status;
+
+typedef enum { VA_F32 = 0, VA_F16 = 1, VA_BF16 = 2, VA_Q8_0 = 3 } va_dtype;
+
+/* Device flag bits (workspace header, read with verify_attn_read_flags). */
+#define VA_FLAG_BAD_CTX 0x1u    /* ctx_lens[s] < B, > max_ctx, or beyond the block table */
+#define VA_FLAG_BAD_PAGE 0x2u   /* block_table entry outside [0, num_pages) */
+#define VA_FLAG_BAD_PARENT 0x4u /* parent[s][i] outside [-1, i) */
+
+typedef struct {
+  int32_t num_seqs;          /* >= 1 */
+  int32_t rows_per_seq;      /* B, 1..64 */
+  int32_t num_q_heads;       /* H */
+  int32_t num_kv_heads;      /* KVH, H % KVH == 0 */
+  int32_t head_dim;          /* D in {64, 128, 256} */
+  int32_t page_size;         /* must be 16 */
+  int32_t num_pages;         /* pool capacity in pages */
+  int32_t max_pages_per_seq; /* block_table row stride */
+  int32_t max_ctx;           /* upper bound of every ctx_lens[s]; sizes the split grid */
+  va_dtype q_dtype;          /* VA_F32 | VA_F16 | VA_BF16 */
+  va_dtype kv_dtype;         /* VA_F16 | VA_Q8_0 */
+  va_dtype out_dtype;        /* VA_F16 | VA_BF16 | VA_F32 */
+  float scale;               /* softmax scale; 0 => 1/sqrt(D) in fp32 */
+  int32_t has_parent;        /* 0: causal rows (parent must be NULL); 1: parent array required */
+} va_problem;
+
+typedef struct va_plan va_plan; /* opaque, host-only, immutable */
+
+/* Read-only summary of a plan (host). */
+typedef struct {
+  int32_t num_splits;        /* S used when verify_attn_run gets num_splits = 0 */
+  int32_t max_splits;        /* largest num_splits the workspace is sized for */
+  int32_t row_groups;        /* workgroups per (sequence, KV head, split) along the rows */
+  int32_t rows_per_group;    /* query rows (drafted row x head of one KV group) per workgroup */
+  int32_t num_cus;           /* compute units the heuristic assumed */
+  int32_t pages_per_split;   /* pages per split at max_ctx with num_splits */
+  size_t workspace_bytes;    /* bytes the caller must provide */
+} va_plan_info;
+
+/*
+ * Validate `problem`, choose the split count and size the workspace.
+ *   problem          (host) copied into the plan
+ *   num_splits       0 = choose from the device's CU count and max_ctx; else the
+ *                    split count to size for (1..256)
+ *   device_ordinal   HIP device whose CU count drives the heuristic
+ *   out_plan         (host) receives the plan; NULL on error
+ *   workspace_bytes  (host, may be NULL) receives the workspace size
+ * Returns VA_OK, VA_EINVAL or VA_EUNSUPPORTED (or VA_EHIP if the device query fails).
+ */
+va_status verify_attn_plan(const va_problem* problem, int32_t num_splits, int32_t device_ordinal,
+                           va_plan** out_plan, size_t* workspace_bytes);
+
+/* Same as verify_attn_plan but with an explicit CU count instead of a device
+ * query (num_cus >= 1).  Host-only; used to test the heuristic without a GPU. */
+va_status verify_attn_plan_for_cus(const va_problem* problem, int32_t num_splits, int32_t num_cus,
+                                   va_plan** out_plan, size_t* workspace_bytes);
+
+/* Fill `info` (host) from a plan. */
+va_status verify_attn_plan_get_info(const va_plan* plan, va_plan_info* info);
+
+void verify_attn_plan_destroy(va_plan* plan);
+
+/*
+ * Run the whole verify attention: the partial kernel, then (num_splits > 1)
+ * the merge kernel; with one split the partial kernel writes out / lse
+ * directly (the "direct" path).
+ *   num_splits  0 = the plan's choice; else 1..max_splits
+ *   workspace   device buffer of at least the plan's workspace_bytes
+ * Pointers as in MEMORY LAYOUTS; k_scale / v_scale must be NULL unless
+ * kv_dtype is VA_Q8_0; parent must be NULL iff has_parent == 0.
+ */
+va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                          const void* k_scale, const void* v_scale, const int32_t* block_table,
+                          const int32_t* ctx_lens, const int32_t* parent, int32_t num_splits,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * The two launches of verify_attn_run, callable separately (same arguments
+ * and checks).  verify_attn_run_partial enqueues only the partial kernel
+ * (with num_splits == 1 it writes out / lse, otherwise the workspace
+ * partials); verify_attn_run_merge enqueues only the merge kernel, reading
+ * the partials a preceding verify_attn_run_partial with the same num_splits
+ * wrote into `workspace` (VA_EINVAL when num_splits == 1).
+ */
+va_status verify_attn_run_partial(const va_plan* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, const void* k_scale, const void* v_scale,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  const int32_t* parent, int32_t num_splits, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+va_status verify_attn_run_merge(const va_plan* plan, int32_t num_splits, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Copy the workspace flag word to *flags (host) after synchronising `stream`,
+ * then clear it on the device.  For tests and debugging; it blocks. */
+va_status verify_attn_read_flags(const va_plan* plan, void* workspace, void* stream, uint32_t* flags);
+
+/* Static description of a status code. */
+const char* verify_attn_status_string(va_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VERIFY_ATTN_H */

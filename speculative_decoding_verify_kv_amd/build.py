@@ -1,0 +1,75 @@
+"""Build libverify_attn.so in-tree with hipcc for gfx950.
+
+Each HIP source is compiled to an object in parallel, then linked into one
+shared library next to this file.  Packed fp32 VALU forms are disabled for
+the device code.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libverify_attn.so")
+SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip"]
+# The partial kernel keeps its O accumulators in VGPRs and lets the Q operand
+# fragments sit in AGPRs (MFMA reads A/B from AGPRs); the default heuristic
+# instead shuttles the accumulators through AGPR spill slots every iteration.
+PER_SOURCE_FLAGS = {"verify_partial.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        "-Wall", "-Wno-unused-function", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
+    ]
+
+
+def _compile(src: str, obj: str, extra=()):
+    cmd = [hipcc(), *_flags(), *PER_SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
+    warn = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    return warn
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every HIP source for gfx950 and link libverify_attn.so (always rebuilds)."""
+    with tempfile.TemporaryDirectory(prefix="va_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+        with cf.ThreadPoolExecutor(jobs) as ex:
+            futs = [ex.submit(_compile, s, o, extra) for s, o in zip(SOURCES, objs)]
+            for f in futs:
+                w = f.result()
+                if verbose and w:
+                    print(w, file=sys.stderr)
+        out_tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("link failed:\n" + r.stderr[-4000:])
+        os.replace(out_tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

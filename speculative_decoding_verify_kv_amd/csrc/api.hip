@@ -1,0 +1,296 @@
+// Host entry points of libverify_attn.so (the C ABI in include/verify_attn.h).
+//
+// Admission is fail-closed, as the page "perf(gfx1100): speed up long-context
+// DFlash verify 13.4% with FA2 split-KV and retain HipGraph/Redline PM4"
+// describes for its split verifier (Default and admission policy; Maintainer
+// review follow-up: the caller-owned partial workspace is checked, an
+// undersized one is refused): every check here returns an error before anything
+// is enqueued, and there is no fallback to another algorithm.
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "va_internal.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+va_status check_problem(const va_problem* p) {
+  if (!p) return VA_EINVAL;
+  if (p->num_seqs < 1 || p->rows_per_seq < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
+      p->num_pages < 1 || p->max_pages_per_seq < 1 || p->max_ctx < 1)
+    return VA_EINVAL;
+  if (p->num_q_heads % p->num_kv_heads) return VA_EINVAL;
+  if (p->rows_per_seq > va::kMaxRows) return VA_EUNSUPPORTED;
+  if (p->page_size != va::kPage) return VA_EUNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return VA_EUNSUPPORTED;
+  if (p->q_dtype != VA_F32 && p->q_dtype != VA_F16 && p->q_dtype != VA_BF16) return VA_EUNSUPPORTED;
+  if (p->kv_dtype != VA_F16 && p->kv_dtype != VA_Q8_0) return VA_EUNSUPPORTED;
+  if (p->out_dtype != VA_F32 && p->out_dtype != VA_F16 && p->out_dtype != VA_BF16) return VA_EUNSUPPORTED;
+  if (p->has_parent != 0 && p->has_parent != 1) return VA_EINVAL;
+  if (!(p->scale >= 0.f) || isinf(p->scale)) return VA_EINVAL;  // negative or NaN
+  if (p->max_ctx < p->rows_per_seq) return VA_EINVAL;
+  if ((int64_t)p->max_ctx > (int64_t)p->max_pages_per_seq * va::kPage) return VA_EINVAL;
+  if ((int64_t)p->num_seqs * p->rows_per_seq * p->num_q_heads > INT32_MAX) return VA_EUNSUPPORTED;
+  return VA_OK;
+}
+
+// Bytes of K plus V (plus scales) one (token, KV head) occupies.
+int64_t kv_bytes_per_token_head(const va_problem& p) {
+  if (p.kv_dtype == VA_Q8_0) return 2 * ((int64_t)p.head_dim + 2 * (p.head_dim / 32));
+  return 2 * 2 * (int64_t)p.head_dim;
+}
+
+// Split-count model.  Work units are (sequence, KV head, row group, split);
+// the partial kernel runs one workgroup per CU.  Size S so that one sequence
+// at max_ctx alone fills every CU, then cap it so that
+//   - every split keeps at least one page pair per wave (8 pages), and
+//   - the fp32 partials written and re-read (S * rows * (D+2) * 4 bytes) stay
+//     below half of the KV bytes streamed, since they cost bandwidth too.
+int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
+  const int64_t units = (int64_t)p.num_kv_heads * t.row_groups;
+  int64_t S = ceil_div(cus, units);
+  const int64_t npages = ceil_div(p.max_ctx, va::kPage);
+  const int64_t s_pages = npages / 8;
+  if (S > s_pages) S = s_pages;
+  const int64_t nrows = (int64_t)p.num_seqs * p.rows_per_seq * p.num_q_heads;
+  const double part_per_split = (double)nrows * (p.head_dim + 2) * 4.0;
+  const double kv = (double)p.num_seqs * p.max_ctx * p.num_kv_heads * kv_bytes_per_token_head(p);
+  const int64_t s_bytes = (int64_t)(0.5 * kv / part_per_split);
+  if (S > s_bytes) S = s_bytes;
+  if (S > va::kMaxSplits) S = va::kMaxSplits;
+  if (S < 1) S = 1;
+  return (int32_t)S;
+}
+
+size_t workspace_for(const va_problem& p, int S) {
+  const size_t nrows = (size_t)p.num_seqs * p.rows_per_seq * p.num_q_heads;
+  if (S <= 1) return va::kHeaderBytes;
+  return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float);
+}
+
+va_status make_plan(const va_problem* problem, int32_t num_splits, int32_t cus, va_plan** out_plan,
+                    size_t* workspace_bytes) {
+  if (out_plan) *out_plan = nullptr;
+  if (!out_plan) return VA_EINVAL;
+  va_status st = check_problem(problem);
+  if (st != VA_OK) return st;
+  if (num_splits < 0 || num_splits > va::kMaxSplits || cus < 1) return VA_EINVAL;
+  const va_problem& p = *problem;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const va::Tiling t = va::choose_tiling(p.rows_per_seq, G, p.head_dim);
+  if (!va::partial_supported(p.head_dim, p.kv_dtype, t.nt)) return VA_EUNSUPPORTED;
+  va_plan* plan = new (std::nothrow) va_plan;
+  if (!plan) return VA_EINVAL;
+  plan->prob = p;
+  plan->tiling = t;
+  plan->num_cus = cus;
+  plan->num_splits = num_splits ? num_splits : heuristic_splits(p, t, cus);
+  plan->max_splits = plan->num_splits;
+  plan->scale = p.scale > 0.f ? p.scale : 1.0f / sqrtf((float)p.head_dim);
+  plan->workspace_bytes = workspace_for(p, plan->max_splits);
+  *out_plan = plan;
+  if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;
+  return VA_OK;
+}
+
+struct RunArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const void* k_scale;
+  const void* v_scale;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* parent;
+};
+
+va_status check_run(const va_plan* plan, const RunArgs& a, int32_t num_splits, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, int32_t* S_out) {
+  if (!plan) return VA_EINVAL;
+  const va_problem& p = plan->prob;
+  if (!a.q || !a.k_pool || !a.v_pool || !a.block_table || !a.ctx_lens || !out || !workspace) return VA_EINVAL;
+  if (!aligned(a.q, 16) || !aligned(a.k_pool, 16) || !aligned(a.v_pool, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 256))
+    return VA_EINVAL;
+  if (!aligned(a.block_table, 4) || !aligned(a.ctx_lens, 4) || (lse && !aligned(lse, 4))) return VA_EINVAL;
+  if (p.kv_dtype == VA_Q8_0) {
+    if (!a.k_scale || !a.v_scale || !aligned(a.k_scale, 16) || !aligned(a.v_scale, 16)) return VA_EINVAL;
+  } else if (a.k_scale || a.v_scale) {
+    return VA_EINVAL;
+  }
+  if ((p.has_parent != 0) != (a.parent != nullptr)) return VA_EINVAL;
+  if (a.parent && !aligned(a.parent, 4)) return VA_EINVAL;
+  const int32_t S = num_splits ? num_splits : plan->num_splits;
+  if (S < 1) return VA_EINVAL;
+  if (S > plan->max_splits) return VA_EWORKSPACE;
+  if (workspace_bytes < plan->workspace_bytes) return VA_EWORKSPACE;
+  *S_out = S;
+  return VA_OK;
+}
+
+va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t S, void* out, float* lse,
+                                 void* workspace) {
+  const va_problem& p = plan->prob;
+  va::PartialParams pp;
+  memset(&pp, 0, sizeof pp);
+  pp.q = a.q;
+  pp.k_pool = a.k_pool;
+  pp.v_pool = a.v_pool;
+  pp.k_scale = a.k_scale;
+  pp.v_scale = a.v_scale;
+  pp.block_table = a.block_table;
+  pp.ctx_lens = a.ctx_lens;
+  pp.parent = a.parent;
+  pp.out = out;
+  pp.lse = lse;
+  const int64_t nrows = (int64_t)p.num_seqs * p.rows_per_seq * p.num_q_heads;
+  char* ws = static_cast<char*>(workspace);
+  pp.flags = reinterpret_cast<uint32_t*>(ws);
+  float* part = reinterpret_cast<float*>(ws + va::kHeaderBytes);
+  pp.part_o = part;
+  pp.part_m = part + (int64_t)plan->max_splits * nrows * p.head_dim;
+  pp.part_l = pp.part_m + (int64_t)plan->max_splits * nrows;
+  pp.num_seqs = p.num_seqs;
+  pp.B = p.rows_per_seq;
+  pp.H = p.num_q_heads;
+  pp.KVH = p.num_kv_heads;
+  pp.G = p.num_q_heads / p.num_kv_heads;
+  pp.D = p.head_dim;
+  pp.num_pages = p.num_pages;
+  pp.max_pages = p.max_pages_per_seq;
+  pp.max_ctx = p.max_ctx;
+  pp.S = S;
+  pp.row_groups = plan->tiling.row_groups;
+  pp.rows_per_group = 16 * plan->tiling.nt;
+  pp.q_dtype = p.q_dtype;
+  pp.out_dtype = p.out_dtype;
+  pp.direct = (S == 1) ? 1 : 0;
+  pp.scale_log2 = plan->scale * 1.4426950408889634f;
+  pp.nrows = nrows;
+  return pp;
+}
+
+va::MergeParams merge_params(const va::PartialParams& pp, void* out, float* lse) {
+  va::MergeParams mp;
+  mp.part_o = pp.part_o;
+  mp.part_m = pp.part_m;
+  mp.part_l = pp.part_l;
+  mp.out = out;
+  mp.lse = lse;
+  mp.S = pp.S;
+  mp.D = pp.D;
+  mp.out_dtype = pp.out_dtype;
+  mp.nrows = pp.nrows;
+  return mp;
+}
+
+}  // namespace
+
+extern "C" {
+
+va_status verify_attn_plan(const va_problem* problem, int32_t num_splits, int32_t device_ordinal,
+                           va_plan** out_plan, size_t* workspace_bytes) {
+  if (out_plan) *out_plan = nullptr;
+  va_status st = check_problem(problem);
+  if (st != VA_OK) return st;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device_ordinal) != hipSuccess) return VA_EHIP;
+  return make_plan(problem, num_splits, prop.multiProcessorCount, out_plan, workspace_bytes);
+}
+
+va_status verify_attn_plan_for_cus(const va_problem* problem, int32_t num_splits, int32_t num_cus,
+                                   va_plan** out_plan, size_t* workspace_bytes) {
+  return make_plan(problem, num_splits, num_cus, out_plan, workspace_bytes);
+}
+
+va_status verify_attn_plan_get_info(const va_plan* plan, va_plan_info* info) {
+  if (!plan || !info) return VA_EINVAL;
+  info->num_splits = plan->num_splits;
+  info->max_splits = plan->max_splits;
+  info->row_groups = plan->tiling.row_groups;
+  info->rows_per_group = 16 * plan->tiling.nt;
+  info->num_cus = plan->num_cus;
+  const int64_t npages = ceil_div(plan->prob.max_ctx, va::kPage);
+  info->pages_per_split = (int32_t)ceil_div(npages, plan->num_splits);
+  info->workspace_bytes = plan->workspace_bytes;
+  return VA_OK;
+}
+
+void verify_attn_plan_destroy(va_plan* plan) { delete plan; }
+
+va_status verify_attn_run_partial(const va_plan* plan, const void* q, const void* k_pool,
+                                  const void* v_pool, const void* k_scale, const void* v_scale,
+                                  const int32_t* block_table, const int32_t* ctx_lens,
+                                  const int32_t* parent, int32_t num_splits, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent};
+  int32_t S = 0;
+  va_status st = check_run(plan, a, num_splits, out, lse, workspace, workspace_bytes, &S);
+  if (st != VA_OK) return st;
+  const va::PartialParams pp = partial_params(plan, a, S, out, lse, workspace);
+  if (va::launch_partial(pp, plan->prob.kv_dtype, plan->tiling.nt, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return VA_EHIP;
+  return VA_OK;
+}
+
+va_status verify_attn_run_merge(const va_plan* plan, int32_t num_splits, void* out, float* lse,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !out || !workspace) return VA_EINVAL;
+  if (!aligned(out, 16) || !aligned(workspace, 256) || (lse && !aligned(lse, 4))) return VA_EINVAL;
+  const int32_t S = num_splits ? num_splits : plan->num_splits;
+  if (S < 2) return VA_EINVAL;
+  if (S > plan->max_splits || workspace_bytes < plan->workspace_bytes) return VA_EWORKSPACE;
+  // Only the workspace layout and the output are needed.
+  const RunArgs none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const va::PartialParams pp = partial_params(plan, none, S, out, lse, workspace);
+  if (va::launch_merge(merge_params(pp, out, lse), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return VA_EHIP;
+  return VA_OK;
+}
+
+va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                          const void* k_scale, const void* v_scale, const int32_t* block_table,
+                          const int32_t* ctx_lens, const int32_t* parent, int32_t num_splits,
+                          void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent};
+  int32_t S = 0;
+  va_status st = check_run(plan, a, num_splits, out, lse, workspace, workspace_bytes, &S);
+  if (st != VA_OK) return st;
+  const va::PartialParams pp = partial_params(plan, a, S, out, lse, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (va::launch_partial(pp, plan->prob.kv_dtype, plan->tiling.nt, s) != hipSuccess) return VA_EHIP;
+  if (S > 1 && va::launch_merge(merge_params(pp, out, lse), s) != hipSuccess) return VA_EHIP;
+  return VA_OK;
+}
+
+va_status verify_attn_read_flags(const va_plan* plan, void* workspace, void* stream, uint32_t* flags) {
+  if (!plan || !workspace || !flags) return VA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return VA_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return VA_EHIP;
+  if (hipMemsetAsync(workspace, 0, sizeof(uint32_t), s) != hipSuccess) return VA_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return VA_EHIP;
+  return VA_OK;
+}
+
+const char* verify_attn_status_string(va_status status) {
+  switch (status) {
+    case VA_OK: return "ok";
+    case VA_EINVAL: return "invalid argument";
+    case VA_EUNSUPPORTED: return "unsupported shape or dtype";
+    case VA_EWORKSPACE: return "workspace too small or too many splits";
+    case VA_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

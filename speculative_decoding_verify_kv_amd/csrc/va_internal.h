@@ -1,0 +1,82 @@
+// Internal declarations shared by the host entry points and the kernel
+// launchers of libverify_attn.so.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "verify_attn.h"
+
+namespace va {
+
+constexpr int kPage = 16;
+constexpr int kWaves = 4;            // waves per workgroup of the partial kernel
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSplits = 256;
+constexpr int kMaxRows = 64;         // B limit (ancestry bitmask width)
+constexpr size_t kHeaderBytes = 256; // workspace flag header
+
+// Kernel-side dtype codes (same values as va_dtype).
+enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kQ8 = 3 };
+
+// Everything a launch needs; passed to the kernels by value.
+struct PartialParams {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const void* k_scale;
+  const void* v_scale;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  const int32_t* parent;  // NULL => chain
+  void* out;              // direct mode output
+  float* lse;             // direct mode lse (may be NULL)
+  float* part_o;          // [S][nrows][D]
+  float* part_m;          // [S][nrows]  (log2 units)
+  float* part_l;          // [S][nrows]
+  uint32_t* flags;
+  int32_t num_seqs, B, H, KVH, G, D;
+  int32_t num_pages, max_pages, max_ctx;
+  int32_t S;              // splits in this launch
+  int32_t row_groups;     // workgroups along the B*G rows of one KV head
+  int32_t rows_per_group; // 16 * NT
+  int32_t q_dtype, out_dtype;
+  int32_t direct;         // 1: write out/lse, 0: write partials
+  float scale_log2;       // softmax scale * log2(e)
+  int64_t nrows;          // num_seqs * B * H
+};
+
+struct MergeParams {
+  const float* part_o;
+  const float* part_m;
+  const float* part_l;
+  void* out;
+  float* lse;
+  int32_t S, D, out_dtype;
+  int64_t nrows;
+};
+
+// Tiling the plan picks for the partial kernel.
+struct Tiling {
+  int nt;          // 16-row MFMA tiles per workgroup (1, 2, 3, 4 or 6)
+  int row_groups;  // ceil(B*G / (16*nt))
+};
+
+Tiling choose_tiling(int B, int G, int D);
+bool partial_supported(int D, int kv_dtype, int nt);
+
+hipError_t launch_partial(const PartialParams& p, int kv_dtype, int nt, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+}  // namespace va
+
+struct va_plan {
+  va_problem prob;
+  int32_t num_splits;       // heuristic (or requested) S
+  int32_t max_splits;       // workspace sized for this many
+  int32_t num_cus;
+  va::Tiling tiling;
+  float scale;              // resolved softmax scale
+  size_t workspace_bytes;
+};

@@ -1,0 +1,273 @@
+"""GPU parity of the HIP verify-attention path against the fp64 oracle.
+
+Every call goes through the C ABI (libverify_attn.so via ctypes).  Inputs are
+the seeded synthetic workloads of `synthetic`; expected values come from the
+oracle only.  Tolerances: relative L2 <= 1e-3 and max-abs <= 2e-3 for fp16 /
+fp32 output (bf16: see gpu_util.check_parity).
+"""
+
+import copy
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+
+from .gpu_util import check_parity, ensure_lib, errors, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+_cache = {}
+
+
+def wl(name):
+    """Module-wide cache of (workload, oracle output, oracle lse)."""
+    if name not in _cache:
+        say(f"[gen] {name}")
+        if name == "tiny_f16":
+            w = S.tiny_dense(kv_dtype="f16")
+        elif name == "qwen_f16_d256":
+            w = S.qwen_dense(ctx=8192, D=256)
+        elif name == "qwen_f16_d128":
+            w = S.qwen_dense(ctx=8192, D=128)
+        elif name.startswith("q8_"):
+            ctx = int(name.split("_")[1])
+            w = S.q8_long(ctx=ctx, permute=name.endswith("perm"))
+        elif name == "paged_ragged":
+            w = S.paged_ragged()
+        elif name == "tree_mixed":
+            w = S.tree_mixed()
+        elif name.startswith("chain_"):
+            _, b, ctx = name.split("_")
+            w = S.chain(int(b), ctx=int(ctx))
+        else:
+            raise KeyError(name)
+        say(f"[oracle] {name}")
+        o, l = oracle.attention(w)
+        _cache[name] = (w, o, l)
+    return _cache[name]
+
+
+# ---------------------------------------------------------------------------
+# parity on the named workloads
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S_", [1, 2, 4])
+@pytest.mark.parametrize("out_dtype", ["f32", "f16", "bf16"])
+def test_tiny_dense(S_, out_dtype):
+    w, o, l = wl("tiny_f16")
+    say(f"[case] tiny_dense S={S_} out={out_dtype}")
+    got, lse, flags, info = run_gpu(w, S_, out_dtype)
+    assert flags == 0
+    check_parity(got, o, out_dtype, f"tiny S={S_}")
+    assert np.abs(lse - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
+
+
+@pytest.mark.parametrize("name", ["qwen_f16_d256", "qwen_f16_d128"])
+@pytest.mark.parametrize("S_", [1, 8, 0])
+def test_qwen_dense_fp16(name, S_):
+    w, o, l = wl(name)
+    say(f"[case] {name} S={S_}")
+    got, lse, flags, info = run_gpu(w, S_, "f16")
+    assert flags == 0
+    check_parity(got, o, "f16", f"{name} S={S_ or info.num_splits}")
+    assert np.abs(lse - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
+
+
+@pytest.mark.parametrize("name", ["q8_8192", "q8_20676", "q8_32768", "q8_32768_perm"])
+@pytest.mark.parametrize("S_", [1, 8, 0])
+def test_q8_long(name, S_):
+    w, o, l = wl(name)
+    say(f"[case] {name} S={S_}")
+    got, lse, flags, info = run_gpu(w, S_, "f16")
+    assert flags == 0
+    check_parity(got, o, "f16", f"{name} S={S_ or info.num_splits}")
+    assert np.abs(lse - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_q8_out_dtypes(out_dtype):
+    w, o, l = wl("q8_8192")
+    say(f"[case] q8_8192 out={out_dtype}")
+    got, lse, flags, info = run_gpu(w, 0, out_dtype)
+    check_parity(got, o, out_dtype, f"q8_8192 out={out_dtype}")
+
+
+@pytest.mark.parametrize("S_", [1, 8, 0])
+def test_paged_ragged(S_):
+    w, o, l = wl("paged_ragged")
+    say(f"[case] paged_ragged S={S_}")
+    got, lse, flags, info = run_gpu(w, S_, "f16")
+    assert flags == 0
+    check_parity(got, o, "f16", f"paged_ragged S={S_ or info.num_splits}")
+    # each sequence on its own as well (the short ones are small next to the 40K one)
+    for s in range(w.num_seqs):
+        rows = slice(s * w.B, (s + 1) * w.B)
+        rel, mx = errors(got[rows], o[rows])
+        assert rel <= 1e-3 and mx <= 2e-3, (s, rel, mx)
+
+
+@pytest.mark.parametrize("S_", [1, 8, 0])
+def test_tree_mixed(S_):
+    w, o, l = wl("tree_mixed")
+    say(f"[case] tree_mixed S={S_} parent={w.parent.tolist()}")
+    got, lse, flags, info = run_gpu(w, S_, "f16")
+    assert flags == 0
+    check_parity(got, o, "f16", f"tree_mixed S={S_ or info.num_splits}")
+
+
+@pytest.mark.parametrize("B", list(range(4, 33)))
+def test_chain_sweep(B):
+    ctx = 20676 if B in (4, 8, 16, 32) else 1500
+    w, o, l = wl(f"chain_{B}_{ctx}")
+    say(f"[case] chain B={B} ctx={ctx}")
+    got, lse, flags, info = run_gpu(w, 0, "f16")
+    assert flags == 0
+    check_parity(got, o, "f16", f"chain B={B}")
+
+
+# ---------------------------------------------------------------------------
+# properties
+# ---------------------------------------------------------------------------
+
+def test_split_entry_points_match_run():
+    w, o, l = wl("q8_8192")
+    say("[case] partial+merge entry points vs run")
+    a = run_gpu(w, 8, "f16")
+    b = run_gpu(w, 8, "f16", entry="split")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_direct_rows_invariant_across_splits():
+    w, o, l = wl("q8_20676")
+    say("[case] direct rows across S")
+    outs = [run_gpu(w, S_, "f32")[0] for S_ in (1, 2, 8, 0)]
+    for x in outs[1:]:
+        rel, mx = errors(x, outs[0])
+        assert rel <= 1e-3 and mx <= 2e-3
+
+
+def test_run_to_run_bitwise():
+    w, o, l = wl("tree_mixed")
+    say("[case] run-to-run determinism")
+    a = run_gpu(w, 0, "f16")
+    b = run_gpu(w, 0, "f16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _repage(w, perm):
+    w2 = copy.deepcopy(w)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    w2.k_pool = np.ascontiguousarray(w.k_pool[inv])
+    w2.v_pool = np.ascontiguousarray(w.v_pool[inv])
+    if w.k_scale is not None:
+        w2.k_scale = np.ascontiguousarray(w.k_scale[inv])
+        w2.v_scale = np.ascontiguousarray(w.v_scale[inv])
+    w2.block_table = perm[w.block_table].astype(np.int32)
+    return w2
+
+
+def test_block_table_permutation_bitwise():
+    w, o, l = wl("tree_mixed")
+    say("[case] block-table permutation")
+    perm = np.random.default_rng(17).permutation(w.num_pages).astype(np.int32)
+    a = run_gpu(w, 0, "f16")
+    b = run_gpu(_repage(w, perm), 0, "f16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_masked_keys_do_not_matter_bitwise():
+    """Rewriting the K/V of keys a row cannot see leaves that row bitwise unchanged."""
+    w, o, l = wl("tree_mixed")
+    say("[case] masked-key perturbation")
+    rng = np.random.default_rng(5)
+    a = run_gpu(w, 0, "f16")[0].reshape(w.num_seqs, w.B, w.H, w.D)
+    ctx = int(w.ctx_lens[0])
+    base = ctx - w.B
+    # tree node rows 2..9: perturb the slot of the last tree node; rows that do
+    # not have it as an ancestor (every row but itself here) must not change
+    last = w.B - 1
+    anc_of = [set() for _ in range(w.B)]
+    for i in range(w.B):
+        j = i
+        while j >= 0:
+            anc_of[i].add(j)
+            j = int(w.parent[0, j])
+    w2 = copy.deepcopy(w)
+    page, slot = int(w.block_table[0, (base + last) // 16]), (base + last) % 16
+    w2.k_pool[page, :, slot, :] = rng.integers(-127, 128, w2.k_pool[page, :, slot, :].shape)
+    w2.v_pool[page, :, :, slot] = rng.integers(-127, 128, w2.v_pool[page, :, :, slot].shape)
+    b = run_gpu(w2, 0, "f16")[0].reshape(a.shape)
+    for i in range(w.B):
+        if last not in anc_of[i]:
+            assert np.array_equal(a[0, i], b[0, i]), i
+    assert not np.array_equal(a[0, last], b[0, last])
+
+
+def test_poisoned_tails_do_not_matter_bitwise():
+    w, o, l = wl("paged_ragged")
+    say("[case] NaN page tails vs zero tails")
+    w0 = S.paged_ragged(poison=False)
+    a = run_gpu(w, 8, "f16")[0]
+    b = run_gpu(w0, 8, "f16")[0]
+    assert np.array_equal(a, b)
+
+
+def test_boundary_1024_direct_rows():
+    """Two direct rows at ctx 1024 versus the same rows plus an 8-node tree at
+    ctx 1032 (64 -> 65 pages): the direct rows see the same keys, so they must
+    agree with each other and with the oracle (the 1,024-token partition
+    boundary of the page 'perf(qwen35): retain speculation during paged
+    prefill', Correctness failure found during qualification)."""
+    say("[case] 1024 boundary")
+    par = S.tree_parent(2, 8, np.random.default_rng(77))
+    wt = S.make_workload("boundary_tree", ctx_lens=[1032], B=10, H=24, KVH=4, D=256, q_dtype="bf16",
+                         kv_dtype="q8_0", seed=31, permute=True, parent=par, spare_pages=3, poison=True)
+    # the direct-only launch: same first 1024 tokens and the same two query rows
+    wd = copy.deepcopy(wt)
+    wd.B = 2
+    wd.parent = None
+    wd.ctx_lens = np.array([1024], np.int32)
+    wd.q = np.ascontiguousarray(wt.q[:2])
+    od, _ = oracle.attention(wd)
+    ot, _ = oracle.attention(wt)
+    assert np.abs(od - ot[:2]).max() <= 1e-12  # the oracle agrees the rows are the same
+    for S_ in (1, 8, 0):
+        gd = run_gpu(wd, S_, "f32")[0]
+        gt = run_gpu(wt, S_, "f32")[0]
+        check_parity(gd, od, "f32", f"direct-only S={S_}")
+        check_parity(gt, ot, "f32", f"direct+tree S={S_}")
+        rel, mx = errors(gt[:2], gd)
+        assert rel <= 1e-3 and mx <= 2e-3, (S_, rel, mx)
+
+
+def test_bad_metadata_sets_flags_and_nans():
+    import speculative_decoding_verify_kv_amd as va
+
+    say("[case] device-side metadata checks")
+    w = S.tree_mixed(ctx=300)
+    bad = copy.deepcopy(w)
+    bad.block_table = bad.block_table.copy()
+    bad.block_table[0, 3] = w.num_pages + 7
+    got, lse, flags, _ = run_gpu(bad, 0, "f16")
+    assert flags & va.VA_FLAG_BAD_PAGE
+    assert np.all(np.isnan(got))
+    bad = copy.deepcopy(w)
+    bad.parent = bad.parent.copy()
+    bad.parent[0, 4] = 4
+    got, lse, flags, _ = run_gpu(bad, 0, "f16")
+    assert flags & va.VA_FLAG_BAD_PARENT
+    assert np.all(np.isnan(got))
+    bad = copy.deepcopy(w)
+    bad.ctx_lens = np.array([w.B - 1], np.int32)
+    got, lse, flags, _ = run_gpu(bad, 1, "f16", plan_splits=1, max_ctx=int(w.ctx_lens[0]))
+    assert flags & va.VA_FLAG_BAD_CTX
+    assert np.all(np.isnan(got))

@@ -1,0 +1,184 @@
+"""Host-only tests of libverify_attn.so: exports, plan validation, the split
+heuristic and workspace sizing, and run-time argument checks that fail
+before anything is launched (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verify_kv_amd as va
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(va.LIB_PATH):
+        from speculative_decoding_verify_kv_amd import build
+
+        build.build()
+    return va.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "verify_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(verify_attn_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(va.EXPORTED)
+
+
+def qwen(**kw):
+    base = dict(num_seqs=1, rows_per_seq=16, num_q_heads=24, num_kv_heads=4, head_dim=256, num_pages=2048,
+                max_pages_per_seq=2048, max_ctx=32768, q_dtype="bf16", kv_dtype="q8_0", out_dtype="f16")
+    base.update(kw)
+    return va.make_problem(**base)
+
+
+def plan_status(problem, splits=0, cus=256):
+    h = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    st = va.load().verify_attn_plan_for_cus(ctypes.byref(problem) if problem is not None else None, splits, cus,
+                                            ctypes.byref(h), ctypes.byref(ws))
+    if st == 0:
+        va.load().verify_attn_plan_destroy(h)
+    else:
+        assert not h.value  # nothing handed out on error
+    return st
+
+
+def test_headline_plan_and_workspace(lib):
+    p = va.verify_attn_plan_for_cus(qwen(), 0, 256)
+    info = p.info()
+    assert info.row_groups == 2 and info.rows_per_group == 48
+    assert info.num_splits == 32 and info.max_splits == 32
+    assert info.pages_per_split == 64
+    nrows = 1 * 16 * 24
+    assert info.workspace_bytes == 256 + 32 * nrows * (256 + 2) * 4
+    assert p.workspace_bytes == info.workspace_bytes
+
+
+@pytest.mark.parametrize("cus", [1, 8, 64, 256, 304])
+def test_heuristic_bounds(lib, cus):
+    p = va.verify_attn_plan_for_cus(qwen(), 0, cus)
+    info = p.info()
+    assert 1 <= info.num_splits <= 256
+    # at least one page pair per wave (8 pages) per split
+    assert info.pages_per_split >= 8
+    # enough splits to fill the CUs when the context allows it
+    assert info.num_splits * 4 * info.row_groups >= min(cus, 4 * info.row_groups * (2048 // 8))
+
+
+def test_explicit_splits_and_direct(lib):
+    p = va.verify_attn_plan_for_cus(qwen(), 8, 256)
+    assert p.info().num_splits == 8 and p.info().max_splits == 8
+    p1 = va.verify_attn_plan_for_cus(qwen(), 1, 256)
+    assert p1.info().workspace_bytes == 256  # direct path needs only the flag header
+
+
+@pytest.mark.parametrize("B,G,D,nt,rg", [(16, 6, 256, 3, 2), (10, 6, 256, 2, 2), (32, 6, 256, 3, 4),
+                                         (4, 6, 256, 2, 1), (16, 6, 128, 6, 1), (4, 2, 64, 1, 1),
+                                         (64, 6, 256, 3, 8), (1, 1, 64, 1, 1)])
+def test_row_tiling(lib, B, G, D, nt, rg):
+    prob = qwen(rows_per_seq=B, num_q_heads=4 * G, head_dim=D)
+    info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
+    assert info.rows_per_group == 16 * nt and info.row_groups == rg
+    assert info.rows_per_group * info.row_groups >= B * G
+
+
+def test_small_context_caps_splits(lib):
+    # page cap binds: 16 pages / 8 pages per split
+    prob = qwen(rows_per_seq=1, num_q_heads=4, head_dim=64, max_ctx=256, max_pages_per_seq=16, num_pages=16)
+    assert va.verify_attn_plan_for_cus(prob, 0, 256).info().num_splits == 2
+    # partial-bytes cap binds: 384 rows of fp32 partials outweigh 256 tokens of KV
+    prob = qwen(max_ctx=256, max_pages_per_seq=16, num_pages=16)
+    assert va.verify_attn_plan_for_cus(prob, 0, 256).info().num_splits == 1
+
+
+def test_partial_bytes_cap(lib):
+    # many equal sequences: the fp32 partials must stay below half of the KV bytes
+    prob = qwen(num_seqs=32, max_ctx=8192, max_pages_per_seq=512, num_pages=32 * 512)
+    info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
+    nrows = 32 * 16 * 24
+    kv = 32 * 8192 * 4 * 2 * (256 + 16)
+    assert info.num_splits * nrows * 258 * 4 <= 0.5 * kv
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=25), va.VA_EINVAL),
+    (dict(head_dim=96), va.VA_EUNSUPPORTED),
+    (dict(rows_per_seq=65), va.VA_EUNSUPPORTED),
+    (dict(page_size=32), va.VA_EUNSUPPORTED),
+    (dict(kv_dtype="f32"), va.VA_EUNSUPPORTED),
+    (dict(kv_dtype="bf16"), va.VA_EUNSUPPORTED),
+    (dict(q_dtype="q8_0"), va.VA_EUNSUPPORTED),
+    (dict(out_dtype="q8_0"), va.VA_EUNSUPPORTED),
+    (dict(max_ctx=32769), va.VA_EINVAL),          # beyond the block table
+    (dict(max_ctx=8), va.VA_EINVAL),              # fewer tokens than drafted rows
+    (dict(scale=-1.0), va.VA_EINVAL),
+    (dict(num_seqs=0), va.VA_EINVAL),
+])
+def test_plan_rejects(lib, kw, status):
+    assert plan_status(qwen(**kw)) == status
+
+
+def test_plan_rejects_null_and_bad_splits(lib):
+    assert plan_status(None) == va.VA_EINVAL
+    assert plan_status(qwen(), splits=257) == va.VA_EINVAL
+    assert plan_status(qwen(), splits=-1) == va.VA_EINVAL
+    assert plan_status(qwen(), cus=0) == va.VA_EINVAL
+
+
+# ---- run-time checks: all fail before any HIP call, so they run without a GPU ----
+
+FAKE = 1 << 20  # 16-byte aligned, never dereferenced on these paths
+
+
+def run_status(plan, **over):
+    a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_scale=FAKE, v_scale=FAKE, block_table=FAKE, ctx_lens=FAKE,
+             parent=None, num_splits=0, out=FAKE, lse=None, workspace=FAKE, workspace_bytes=plan.workspace_bytes)
+    a.update(over)
+    return va.verify_attn_run(plan, a["q"], a["k_pool"], a["v_pool"], a["k_scale"], a["v_scale"],
+                              a["block_table"], a["ctx_lens"], a["parent"], a["num_splits"], a["out"], a["lse"],
+                              a["workspace"], a["workspace_bytes"], None, raise_on_error=False)
+
+
+def test_run_rejects_bad_arguments(lib):
+    plan = va.verify_attn_plan_for_cus(qwen(), 8, 256)
+    assert run_status(plan, workspace_bytes=plan.workspace_bytes - 1) == va.VA_EWORKSPACE
+    assert run_status(plan, num_splits=9) == va.VA_EWORKSPACE
+    assert run_status(plan, num_splits=-2) == va.VA_EINVAL
+    assert run_status(plan, q=None) == va.VA_EINVAL
+    assert run_status(plan, out=None) == va.VA_EINVAL
+    assert run_status(plan, workspace=None) == va.VA_EINVAL
+    assert run_status(plan, k_scale=None) == va.VA_EINVAL        # Q8 needs scales
+    assert run_status(plan, q=FAKE + 8) == va.VA_EINVAL          # misaligned
+    assert run_status(plan, workspace=FAKE + 16) == va.VA_EINVAL
+    assert run_status(plan, parent=FAKE) == va.VA_EINVAL         # has_parent == 0
+    assert run_status(plan, block_table=FAKE + 2) == va.VA_EINVAL
+    plan_p = va.verify_attn_plan_for_cus(qwen(has_parent=True), 8, 256)
+    assert run_status(plan_p) == va.VA_EINVAL                    # parent required
+    plan_f16 = va.verify_attn_plan_for_cus(qwen(kv_dtype="f16"), 8, 256)
+    assert run_status(plan_f16) == va.VA_EINVAL                  # fp16 KV takes no scales
+
+
+def test_merge_entry_checks(lib):
+    plan = va.verify_attn_plan_for_cus(qwen(), 8, 256)
+    f = va.verify_attn_run_merge
+    assert f(plan, 1, FAKE, None, FAKE, plan.workspace_bytes, None, raise_on_error=False) == va.VA_EINVAL
+    assert f(plan, 9, FAKE, None, FAKE, plan.workspace_bytes, None, raise_on_error=False) == va.VA_EWORKSPACE
+    assert f(plan, 8, FAKE, None, FAKE, 100, None, raise_on_error=False) == va.VA_EWORKSPACE
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert va.verify_attn_status_string(st)
+    assert va.verify_attn_status_string(-99) == "unknown status"
