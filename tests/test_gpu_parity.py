@@ -14,7 +14,7 @@ import pytest
 import oracle
 import synthetic as S
 
-from .gpu_util import check_parity, ensure_lib, errors, run_gpu, say
+from .gpu_util import check_bf16_rounding, check_parity, ensure_lib, errors, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,8 @@ def test_tiny_dense(S_, out_dtype):
     assert flags == 0
     check_parity(got, o, out_dtype, f"tiny S={S_}")
     assert np.abs(lse - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
+    if out_dtype == "bf16":
+        check_bf16_rounding(w, o, S_)
 
 
 @pytest.mark.parametrize("name", ["qwen_f16_d256", "qwen_f16_d128"])
@@ -98,6 +100,9 @@ def test_q8_out_dtypes(out_dtype):
     say(f"[case] q8_8192 out={out_dtype}")
     got, lse, flags, info = run_gpu(w, 0, out_dtype)
     check_parity(got, o, out_dtype, f"q8_8192 out={out_dtype}")
+    if out_dtype == "bf16":
+        check_bf16_rounding(w, o, 0)
+        check_bf16_rounding(w, o, 1)
 
 
 @pytest.mark.parametrize("S_", [1, 8, 0])
@@ -215,7 +220,19 @@ def test_masked_keys_do_not_matter_bitwise():
 def test_poisoned_tails_do_not_matter_bitwise():
     w, o, l = wl("paged_ragged")
     say("[case] NaN page tails vs zero tails")
-    w0 = S.paged_ragged(poison=False)
+    # same arrays with every slot that holds no token zeroed instead of poisoned
+    w0 = copy.deepcopy(w)
+    valid = np.zeros((w.num_pages, 16), bool)
+    for s in range(w.num_seqs):
+        c = int(w.ctx_lens[s])
+        tok = np.arange(c)
+        valid[w.block_table[s, tok // 16], tok % 16] = True
+    pg, sl = np.nonzero(~valid)
+    w0.k_pool[pg, :, sl, :] = 0
+    w0.v_pool[pg, :, :, sl] = 0
+    w0.k_scale[pg, :, sl, :] = 0
+    w0.v_scale[pg, :, :, sl] = 0
+    assert np.isnan(w.k_scale[pg, :, sl, :].astype(np.float32)).all()
     a = run_gpu(w, 8, "f16")[0]
     b = run_gpu(w0, 8, "f16")[0]
     assert np.array_equal(a, b)
