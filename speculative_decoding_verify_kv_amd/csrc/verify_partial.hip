@@ -442,18 +442,8 @@ __global__ __launch_bounds__(256, 1) void verify_partial_kernel(const PartialPar
         const uint32_t krow = st + G::K_OFF + sl * G::KPAGE + t * G::KROW;
         const uint32_t srow = st + G::KS_OFF + sl * G::SPAGE + t * (D / 32) * 2;
         h16 kscale[D / 64];
-        if constexpr (D == 256) {
-          const h16x8 sc = *LDS_PTR(h16x8, srow);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) kscale[j] = sc[2 * j + (g4 >> 1)];
-        } else if constexpr (D == 128) {
-          const h16x4 sc = *LDS_PTR(h16x4, srow);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) kscale[j] = sc[2 * j + (g4 >> 1)];
-        } else {
-          const h16x2 sc = *LDS_PTR(h16x2, srow);
-          kscale[0] = sc[g4 >> 1];
-        }
+        for (int j = 0; j < D / 64; ++j) kscale[j] = *LDS_PTR(h16, srow + 2 * (2 * j + (g4 >> 1)));
 #pragma unroll
         for (int j = 0; j < D / 64; ++j) {
           const int c = 4 * j + g4;
@@ -514,9 +504,8 @@ __global__ __launch_bounds__(256, 1) void verify_partial_kernel(const PartialPar
       float mx = sv[nt][0];
 #pragma unroll
       for (int e = 1; e < KPL; ++e) mx = fmaxf(mx, sv[nt][e]);
-      mx = wave_max16(mx) * c2;  // tile max in log2 units (c2 > 0)
-      tmax[nt] = mx;
-      need |= mx > m_run[nt] + kLazyRescale;
+      tmax[nt] = mx * c2;
+      need |= tmax[nt] > m_run[nt] + kLazyRescale;
     }
     return __builtin_amdgcn_ballot_w64(need) != 0;
   };
@@ -524,7 +513,7 @@ __global__ __launch_bounds__(256, 1) void verify_partial_kernel(const PartialPar
   // Raise every row's reference max to the largest scaled score seen so far.
   auto raise_reference = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) m_run[nt] = fmaxf(m_run[nt], tmax[nt]);
+    for (int nt = 0; nt < NT; ++nt) m_run[nt] = fmaxf(m_run[nt], wave_max16(tmax[nt]));
   };
 
   // Phase 2: P = 2^(t - m_ref) in fp16 (registers only), O^T += V^T P^T.
