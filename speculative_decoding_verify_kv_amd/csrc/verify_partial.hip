@@ -1,29 +1,40 @@
 // Split-KV partial kernel for speculative-decoding verify attention, gfx950.
 //
 // One workgroup = (sequence s, KV head, split k, row group).  Its rows are
-// 16*NT (drafted row, query head) pairs of one KV group: because every query
-// head of a GQA group reads the same KV head, the group's B*G rows form the M
-// side of a real matrix product with the streamed keys, so each fetched KV
-// byte feeds many rows (the multi-row verifier idea of the page "perf(gfx11):
-// optimize Qwen DFlash speculative verify", alpineQ's notes, taken to the whole
-// group).  The split's pages are dealt to the 4 waves in pairs; each wave runs
-// an independent online softmax over its pages and the waves are merged
-// through LDS at the end, so the hot loop has no barrier.
+// 16*NT (query head, drafted row) pairs of one KV group: every query head of
+// a GQA group reads the same KV head, so the group's B*G rows form the N side
+// of a real matrix product with the streamed keys and each fetched KV byte
+// feeds all of them (the multi-row verifier idea of the page "perf(gfx11):
+// optimize Qwen DFlash speculative verify", alpineQ's notes, taken to the
+// whole group).
 //
-// Per wave iteration (Q8: two 16-token pages = 32 keys; fp16: one page):
-//   1. LDS-DMA (global_load_lds_dwordx4) of the NEXT iteration's K page(s), V
-//      page(s) and scales into the wave's other ring stage (no VGPRs hold
-//      in-flight data; the wave only waits on its own vmcnt).
-//   2. K fragments from LDS -> int8 to fp16 dequant in registers -> S^T = K Q^T
-//      on v_mfma_f32_16x16x32_f16 (keys on M, rows on N, fp32 accumulate).
-//   3. Causal / tree / page-tail masking by select (only on iterations that
-//      reach the drafted suffix or the split end), online softmax in the log2
-//      domain with lazily rescaled running max, P packed to fp16.
-//   4. V^T fragments (dim-major pages: 8 tokens of one dim are contiguous) ->
-//      dequant -> O^T += V^T P^T on MFMA.  The S^T accumulator layout is
-//      already the P^T operand layout, so P never leaves registers.
-// Epilogue: (m, l) exchange, O rescale, reduce-scatter of O across waves
-// through LDS, then either fp32 partials (split) or the final output (direct).
+// The workgroup has 8 waves in two roles, one of each role per SIMD, so that
+// one wave's matrix-core work overlaps the other's vector work:
+//   score waves p = 0..3   each owns page p of every 64-key tile: LDS-DMA of
+//                          that page's K (and scales), int8 -> fp16 dequant,
+//                          S^T = K Q^T on v_mfma_f32_16x16x32_f16 (keys on M,
+//                          rows on N, Q resident in registers), causal / tree /
+//                          page-tail mask, P = 2^(t - m_ref) in fp16 -> LDS.
+//   output waves q = 0..3  each owns head_dim quarter q: LDS-DMA of that
+//                          quarter of the tile's V (and one page's scales),
+//                          dequant, O^T += V^T P^T on the same MFMA, with P of
+//                          the previous tile read from LDS.
+// Every KV element is therefore dequantised once per workgroup, and O lives
+// in exactly one wave, so the epilogue needs no cross-wave O reduction.
+//
+// Pipeline: separate K and V rings of R stages, filled by
+// global_load_lds_dwordx4 (no VGPR holds data in flight).  Iteration i: score
+// waves compute tile i while output waves accumulate tile i-1; one barrier per
+// iteration.  K of tile i + R - 1 and V of tile i + R - 2 are issued at the
+// start of iteration i, each wave issuing the same number of DMA instructions
+// and waiting only on its own vmcnt before the barrier.
+//
+// Softmax: log2 domain with a reference max per row held by every wave.  A
+// score may exceed its row's reference by at most 15 (P stays within fp16);
+// when one does (always on the first tile), all waves take a short rare path
+// after the barrier: the score waves publish the tile's row maxima, every wave
+// raises the reference, the output waves rescale O, the score waves rescale l
+// and rewrite the tile's P.
 //
 // Split partials + log-sum-exp merge and "S1 is the direct path" follow the
 // page "perf(gfx1100): speed up long-context DFlash verify 13.4% with FA2
@@ -53,12 +64,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, off) (reinterpret_cast<__attribute__((address_space(3))) T*>(off))
 
+constexpr int kRoleWaves = 4;                      // score waves; as many output waves
+constexpr int kBlockThreads = 64 * 2 * kRoleWaves;  // 512
 constexpr float kLazyRescale = 15.0f;  // 2^15 < 65504: the largest P value fp16 holds safely
+constexpr float kFiniteFloor = -1e30f;  // stands for an unset (-inf) reference in differences
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---- LDS-DMA helpers -------------------------------------------------------
-// global_load_lds_dwordx4: each active lane copies 16 bytes from its global
-// address to LDS at M0 + 16 * lane.  M0 is saved and restored around it.
+// global_load_lds_dword[x4]: each active lane copies 4 (16) bytes from its
+// global address to LDS at M0 + 4 (16) * lane.  M0 is saved and restored.
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
@@ -66,7 +80,6 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 
-// sbase and lds must be wave-uniform; readfirstlane makes that explicit.
 __device__ __forceinline__ void dma_saddr(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
   const void* sbase = uniform_ptr(sbase_in);
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
@@ -96,49 +109,86 @@ __device__ __forceinline__ void dma_vaddr(const void* vaddr, uint32_t lds_in) {
       : "memory");
 }
 
+__device__ __forceinline__ void dma_saddr_b32(const void* sbase_in, uint32_t voff, uint32_t lds_in) {
+  const void* sbase = uniform_ptr(sbase_in);
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_in);
+  uint32_t keep;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(keep)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// ---- geometry of one wave's ring stage --------------------------------------
+// Wait until at most n * PER of this wave's vector-memory loads are in flight.
+template <int PER>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<2 * PER>();
+}
+
+// Workgroup barrier that makes this wave's LDS writes visible; it does not
+// wait for in-flight global loads (the ring waits on vmcnt itself).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---- geometry ------------------------------------------------------------------
 template <int D, int KVT>
 struct Geo {
   static constexpr bool Q8 = (KVT == kQ8);
-  static constexpr int PPI = Q8 ? 2 : 1;         // pages per wave iteration
-  static constexpr int ESZ = Q8 ? 1 : 2;         // bytes per K/V element
-  static constexpr int KROW = D * ESZ;            // bytes of one token's K
+  static constexpr int ESZ = Q8 ? 1 : 2;          // bytes per K/V element
+  static constexpr int KROW = D * ESZ;            // bytes of one token's K row
   static constexpr int KPAGE = 16 * KROW;         // K bytes of one page (one KV head)
-  static constexpr int VPAGE = D * 16 * ESZ;      // V bytes of one page
-  static constexpr int SPAGE = Q8 ? D : 0;       // bytes of one page's K (or V) scales
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = PPI * KPAGE;
-  static constexpr int KS_OFF = V_OFF + PPI * VPAGE;
-  static constexpr int VS_OFF = KS_OFF + PPI * SPAGE;
-  static constexpr int STAGE = VS_OFF + PPI * SPAGE;
-  static constexpr int KCH = KROW / 16;           // 16-byte chunks per K token row
-  static constexpr int K_DMA = KPAGE / 1024;      // 1 KB DMA instructions per K page
-  static constexpr int V_DMA = VPAGE / 1024;
-  static constexpr int S_LANES = Q8 ? (4 * SPAGE) / 16 : 0;
-  static constexpr int NDMA = PPI * (K_DMA + V_DMA) + (Q8 ? 1 : 0);
-  static constexpr int MT = D / 16;               // 16-dim tiles of O
-  static_assert(KPAGE % 1024 == 0 && VPAGE % 1024 == 0, "page must be whole KB");
-  static_assert(S_LANES <= 64, "scale DMA fits one instruction");
+  static constexpr int KCH = KPAGE / 1024;        // 1 KB chunks of a K page
+  static constexpr int SPB = Q8 ? D : 0;          // bytes of one page's K (or V) scales
+  static constexpr int VROW = 16 * ESZ;           // bytes of one dim row (16 tokens) of a V page
+  static constexpr int VPAGE = D * VROW;
+  static constexpr int DO = D / 4;                // head_dim entries per output wave
+  static constexpr int MTO = DO / 16;             // 16-dim tiles per output wave
+  static constexpr int VCH = MTO * (VROW / 16);   // 1 KB V chunks per output wave per tile
+  static constexpr int NDMA = KCH + (Q8 ? 1 : 0); // DMA instructions per wave per tile
+  static constexpr int K_STAGE = 4 * KPAGE + 4 * SPB;
+  static constexpr int V_STAGE = 4 * VPAGE + 4 * SPB;
+  static constexpr int KSTEPS = D / 32;
+  static_assert(KCH == VCH, "score and output waves issue the same number of DMAs");
+  static_assert(KPAGE % 1024 == 0, "page must be whole KB");
 };
 
-// XOR swizzle of the 16-byte chunk position inside a K token row in LDS, so
-// the lanes that read one fragment hit distinct banks.
-template <int D, int KVT>
-__device__ __forceinline__ int kswz(int t, int slot) {
-  constexpr int KCH = Geo<D, KVT>::KCH;
-  if constexpr (KVT == kQ8) {
-    int v = (t & 3) | (((t >> 3) & 1) << 2) | (((t >> 2) & 1) << 3);
-    return (v ^ (slot << 3)) & (KCH - 1);
-  } else {
-    return t & (KCH - 1);
-  }
-}
+template <int D, int KVT, int NT>
+struct Lay {
+  using G = Geo<D, KVT>;
+  static constexpr int P_BUF = 2 * NT * 1024;  // one tile's P: [h][nt][lane] x 16 B
+  static constexpr int MISC = 512 + 512 + 4 * 16 * NT * 4 + 16;
+  static constexpr int BUDGET = 160 * 1024;
+  static constexpr int PAIR = G::K_STAGE + G::V_STAGE;
+  static constexpr int R = (4 * PAIR + 2 * P_BUF + MISC <= BUDGET) ? 4 : (3 * PAIR + 2 * P_BUF + MISC <= BUDGET) ? 3 : 2;
+  static constexpr int KR_OFF = 0;
+  static constexpr int VR_OFF = R * G::K_STAGE;
+  static constexpr int P_OFF = VR_OFF + R * G::V_STAGE;
+  static constexpr int IDS_OFF = P_OFF + 2 * P_BUF;  // int32 [2][64] page ids
+  static constexpr int ANC_OFF = IDS_OFF + 512;      // uint64 [64] ancestry masks
+  static constexpr int EX_OFF = ANC_OFF + 512;       // float [4][16 NT] row exchange
+  static constexpr int FLAG_OFF = EX_OFF + 4 * 16 * NT * 4;  // int flags [3]
+  static constexpr int BYTES = FLAG_OFF + 16;
+  // Q staging (fp16 [16 NT][D]) during the prologue: V stages R-2 and R-1
+  // receive nothing before the first iteration, so the first K/V pages can
+  // already be in flight while Q is converted; otherwise the ring start.
+  static constexpr int QST_BYTES = 16 * NT * D * 2;
+  static constexpr bool EARLY = QST_BYTES <= 2 * G::V_STAGE;
+  static constexpr int QST_OFF = EARLY ? VR_OFF + (R - 2) * G::V_STAGE : 0;
+  static_assert(BYTES <= BUDGET, "LDS budget");
+  static_assert(EARLY || QST_BYTES <= P_OFF, "Q staging fits the rings");
+};
 
 // ---- numeric helpers ---------------------------------------------------------
 __device__ __forceinline__ h16x2 as_h2(uint32_t u) { return __builtin_bit_cast(h16x2, u); }
@@ -158,6 +208,14 @@ __device__ __forceinline__ h16x8 cat(h16x2 a, h16x2 b, h16x2 c, h16x2 d) {
   r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
   r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
   return r;
+}
+
+// Two dwords of int8 (8 values) times per-pair scales -> one MFMA fragment.
+__device__ __forceinline__ h16x8 deq8(uint32_t w0, uint32_t w1, h16x2 s0, h16x2 s1, h16x2 s2, h16x2 s3) {
+  h16x2 a, b, c, d;
+  i8x4_to_h(w0, a, b);
+  i8x4_to_h(w1, c, d);
+  return cat(a * s0, b * s1, c * s2, d * s3);
 }
 
 __device__ __forceinline__ h16x8 load_q8(const void* q, int dtype, int64_t elem) {
@@ -205,43 +263,53 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Keep-mask for 8 consecutive tokens starting at `first`: fp16 lanes of
+// tokens at or past `end` are cleared (their pages may hold anything).
+__device__ __forceinline__ u32x4 tail_mask(int first, int end) {
+  u32x4 m;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2)
+    m[e2] = (first + 2 * e2 < end ? 0x0000ffffu : 0u) | (first + 2 * e2 + 1 < end ? 0xffff0000u : 0u);
+  return m;
+}
+
 // ---- the kernel -------------------------------------------------------------
 template <int D, int KVT, int NT>
-struct Smem {
+__global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const PartialParams p) {
   using G = Geo<D, KVT>;
-  static constexpr int RING = kWaves * 2 * G::STAGE;
-  static constexpr int QUARTER = (G::MT / 4) * NT * 1024;  // one wave's O slice for one dim quarter
-  static constexpr int EPI = 12 * QUARTER;                   // 4 destinations x 3 sources
-  static constexpr int BIG = RING > EPI ? RING : EPI;
-  static constexpr int ML_OFF = BIG;                         // float2 (m, l) per (wave, row)
-  static constexpr int POISON_OFF = ML_OFF + kWaves * 16 * NT * 8;
-  static constexpr int ANC_OFF = POISON_OFF + 16;               // uint64 ancestry mask per drafted row
-  static constexpr int BYTES = ANC_OFF + kMaxRows * 8;
-};
-
-template <int D, int KVT, int NT>
-__global__ __launch_bounds__(256, 1) void verify_partial_kernel(const PartialParams p) {
-  using G = Geo<D, KVT>;
-  using SM = Smem<D, KVT, NT>;
-  static_assert(SM::BYTES <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) char smem[SM::BYTES];
-
-  constexpr int KSTEPS = D / 32;  // k-steps of 32 dims in Q K^T
-  constexpr int MT = G::MT;
+  using L = Lay<D, KVT, NT>;
+  constexpr int R = L::R;
+  constexpr int KSTEPS = G::KSTEPS;
+  constexpr int NDMA = G::NDMA;
+  constexpr int QROWS = 16 * NT;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m16 = lane & 15;  // M index (key / dim) or N index (row) within a 16x16 tile
+  const bool is_score = wave < kRoleWaves;
+  const int role = is_score ? wave : wave - kRoleWaves;  // page (score) or dim quarter (output)
+  const int n16 = lane & 15;  // M or N index within a 16x16 tile
   const int g4 = lane >> 4;   // lane group
 
+  // Workgroup -> (split, row group).  When every split has several row
+  // groups, the row groups of one split get block ids 8 apart: blocks are
+  // dealt round-robin to the 8 XCDs, so they share one L2 and run together.
   const int s = blockIdx.z;
   const int kvh = blockIdx.y;
-  const int split = blockIdx.x % p.S;
-  const int rg = blockIdx.x / p.S;
+  int split, rg;
+  if (p.row_groups > 1 && (p.S & 7) == 0) {
+    const int x = blockIdx.x, hi = x >> 3;
+    rg = hi % p.row_groups;
+    split = (hi / p.row_groups) * 8 + (x & 7);
+  } else {
+    split = blockIdx.x % p.S;
+    rg = blockIdx.x / p.S;
+  }
   const int B = p.B;
   const int M = B * p.G;
-  const int rowbase = rg * p.rows_per_group;
+  const int rowbase = rg * QROWS;
 
   // ---- validate sequence metadata (device-resident) ----
   int ctx = p.ctx_lens[s];
@@ -264,17 +332,123 @@ __global__ __launch_bounds__(256, 1) void verify_partial_kernel(const PartialPar
   }
   const int base = ctx - B;  // slot of drafted row 0
 
-  // ---- prologue through LDS: Q rows as fp16 and per-row ancestry masks ----
-  // The ring is not in use yet, so its first bytes stage the workgroup's Q
-  // tile [16*NT rows][D] (fp16, row-major) and the B ancestry bitmasks.
-  constexpr int QROWS = 16 * NT;
-  h16* q_lds = reinterpret_cast<h16*>(smem);
-  uint64_t* anc_lds = reinterpret_cast<uint64_t*>(smem + SM::ANC_OFF);
-  static_assert(QROWS * D * 2 <= SM::RING, "prologue staging fits the ring");
+  // ---- this split's pages and tiles of 4 pages ----
+  const int npages = (ctx + kPage - 1) / kPage;
+  const int pps = (npages + p.S - 1) / p.S;
+  const int p_begin = min(split * pps, npages);
+  const int p_end = min(p_begin + pps, npages);
+  const int npg = p_end - p_begin;
+  const int T = (npg + 3) >> 2;
+  const int split_end = min(ctx, p_end * kPage);
+  const int mask_from = min(base, split_end);  // first token that needs a per-key test
+  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_pages;
+
+  int* ids_lds = reinterpret_cast<int*>(smem + L::IDS_OFF);
+  uint64_t* anc_lds = reinterpret_cast<uint64_t*>(smem + L::ANC_OFF);
+  float* ex_lds = reinterpret_cast<float*>(smem + L::EX_OFF);
+  // [0], [1]: overflow flag of even / odd iterations (double-buffered so a
+  // score wave that runs ahead cannot set the flag a slow reader is reading);
+  // [2]: some wave saw an out-of-range page id.
+  auto flag_ref = [&](int idx) __attribute__((always_inline)) -> volatile __attribute__((address_space(3))) int& {
+    return *LDS_PTR(volatile int, lds0 + L::FLAG_OFF + 4 * idx);
+  };
+  // wave-uniform read of a flag after a barrier
+  auto flag_set = [&](int idx) __attribute__((always_inline)) -> bool {
+    return __builtin_amdgcn_readfirstlane(flag_ref(idx)) != 0;
+  };
+
+  // ---- prologue 1: page ids of the first 128 pages, ancestry masks ----
+  if (tid < 128) ids_lds[tid] = (tid < npg) ? bt_row[p_begin + tid] : 0;
+  if (tid < B) {
+    uint64_t a = 0;
+    int i = tid;
+    for (int guard = 0; guard < kMaxRows && i >= 0; ++guard) {
+      a |= (uint64_t)1 << i;
+      const int par = p.parent ? p.parent[(int64_t)s * B + i] : i - 1;
+      i = (par < i) ? par : -1;  // a malformed parent is flagged above; stop the walk
+    }
+    anc_lds[tid] = poison ? 0 : a;
+  }
+  if (tid == 0) {
+    flag_ref(0) = 0;
+    flag_ref(1) = 0;
+    flag_ref(2) = 0;
+  }
+  __syncthreads();
+
+  // ---- DMA issue ----
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * G::KPAGE;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * G::VPAGE;
+  const char* ksbase = reinterpret_cast<const char*>(p.k_scale) + (int64_t)kvh * G::SPB;
+  const char* vsbase = reinterpret_cast<const char*>(p.v_scale) + (int64_t)kvh * G::SPB;
+  const int64_t kstride = (int64_t)p.KVH * G::KPAGE;  // bytes between pages
+  const int64_t vstride = (int64_t)p.KVH * G::VPAGE;
+  const int64_t sstride = (int64_t)p.KVH * G::SPB;
+  bool bad_page = false;
+
+  // Physical id of split page `off` (per lane).  Padding pages past the split
+  // end read page 0 and are masked; an out-of-range id is flagged and replaced.
+  auto page_id = [&](int off) __attribute__((always_inline)) -> int {
+    if (off >= npg) return 0;
+    int id = ids_lds[((off >> 6) & 1) * 64 + (off & 63)];
+    if (id < 0 || id >= p.num_pages) {
+      bad_page = true;
+      id = 0;
+    }
+    return id;
+  };
+
+  // Score wave p: K page p of tile j (4 KB chunks; lane (g, m) of chunk c
+  // carries token m, bytes [64c + 16g, 64c + 16g + 16)), plus its scales.
+  auto issue_k = [&](int j) __attribute__((always_inline)) {
+    const int id = __builtin_amdgcn_readfirstlane(page_id(4 * j + role));
+    const uint32_t st = lds0 + L::KR_OFF + (j % R) * G::K_STAGE;
+    const char* src = kbase + (int64_t)id * kstride;
+    const uint32_t voff = n16 * G::KROW + 16 * g4;
+#pragma unroll
+    for (int c = 0; c < G::KCH; ++c) dma_saddr(src + 64 * c, voff, st + role * G::KPAGE + 1024 * c);
+    if constexpr (G::Q8) {
+      if (lane < D / 16) dma_saddr(ksbase + (int64_t)id * sstride, 16 * lane, st + 4 * G::KPAGE + role * D);
+    }
+  };
+
+  // Output wave q: dims [q*DO, q*DO + DO) of all 4 pages of tile j (lane
+  // (g, m) of chunk (mt, hh) carries page g, dim q*DO + 16mt + m, bytes
+  // [16hh, 16hh + 16) of its 16-token row), plus page q's V scales.
+  auto issue_v = [&](int j) __attribute__((always_inline)) {
+    const int id = page_id(4 * j + g4);
+    const uint32_t st = lds0 + L::VR_OFF + (j % R) * G::V_STAGE;
+    const char* src = vbase + (int64_t)id * vstride + (int64_t)(role * G::DO + n16) * G::VROW;
+#pragma unroll
+    for (int mt = 0; mt < G::MTO; ++mt)
+#pragma unroll
+      for (int hh = 0; hh < G::VROW / 16; ++hh)
+        dma_vaddr(src + 16 * mt * G::VROW + 16 * hh, st + (role * G::VCH + mt * (G::VROW / 16) + hh) * 1024);
+    if constexpr (G::Q8) {
+      const int idq = __builtin_amdgcn_readlane(id, 16 * role);
+      if (lane < D / 16) dma_saddr(vsbase + (int64_t)idq * sstride, 16 * lane, st + 4 * G::VPAGE + role * D);
+    }
+  };
+
+  auto prologue_dma = [&]() __attribute__((always_inline)) {
+    if (is_score) {
+#pragma unroll
+      for (int j = 0; j < R - 1; ++j)
+        if (j < T) issue_k(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < R - 2; ++j)
+        if (j < T) issue_v(j);
+    }
+  };
+
+  if constexpr (L::EARLY) prologue_dma();
+
+  // ---- prologue 2: Q rows of this group as fp16 through LDS ----
+  h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
   {
-    // 8 consecutive elements per thread per step
     constexpr int CH = D / 8;
-    for (int idx = tid; idx < QROWS * CH; idx += kThreads) {
+    for (int idx = tid; idx < QROWS * CH; idx += kBlockThreads) {
       const int rr = idx / CH, c8 = idx % CH;
       const int r = rowbase + rr;
       h16x8 v = h16x8{};
@@ -285,475 +459,336 @@ __global__ __launch_bounds__(256, 1) void verify_partial_kernel(const PartialPar
       }
       *reinterpret_cast<h16x8*>(q_lds + rr * D + 8 * c8) = v;
     }
-    if (tid < B) {
-      uint64_t a = 0;
-      int i = tid;
-      for (int guard = 0; guard < kMaxRows && i >= 0; ++guard) {
-        a |= (uint64_t)1 << i;
-        const int par = p.parent ? p.parent[(int64_t)s * B + i] : i - 1;
-        i = (par < i) ? par : -1;  // a malformed parent is flagged above; stop the walk
-      }
-      anc_lds[tid] = poison ? 0 : a;
-    }
   }
   __syncthreads();
-  h16x8 qf[NT][KSTEPS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int rr = 16 * nt + m16;
-    const int r = rowbase + rr;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      int dim0;
-      if constexpr (KVT == kQ8) dim0 = 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1);
-      else dim0 = 32 * ks + 8 * g4;
-      qf[nt][ks] = *reinterpret_cast<const h16x8*>(q_lds + rr * D + dim0);
-    }
-  }
-  __syncthreads();  // the ring may now overwrite the staging area
 
-  // ---- this split's pages ----
-  const int npages = (ctx + kPage - 1) / kPage;
-  const int pps = (npages + p.S - 1) / p.S;
-  const int p_begin = min(split * pps, npages);
-  const int p_end = min(p_begin + pps, npages);
-  const int split_end = min(ctx, p_end * kPage);
-  const int mask_from = min(base, split_end);  // first token that needs a per-key test
-  const int npairs = (p_end - p_begin + G::PPI - 1) / G::PPI;
-  const int n_my = npairs > wave ? (npairs - wave + kWaves - 1) / kWaves : 0;
-  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_pages;
+  const float c2 = p.scale_log2;
+  const int fbuf = L::P_BUF;  // bytes of one P buffer
 
-  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * G::KPAGE;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * G::VPAGE;
-  const char* ksbase = reinterpret_cast<const char*>(p.k_scale) + (int64_t)kvh * G::SPAGE;
-  const char* vsbase = reinterpret_cast<const char*>(p.v_scale) + (int64_t)kvh * G::SPAGE;
-  const int64_t kstride = (int64_t)p.KVH * G::KPAGE;  // bytes between pages
-  const int64_t vstride = (int64_t)p.KVH * G::VPAGE;
-  const int64_t sstride = (int64_t)p.KVH * G::SPAGE;
-
-  const uint32_t lds_ring = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
-  const uint32_t my_ring = __builtin_amdgcn_readfirstlane(lds_ring + wave * 2 * G::STAGE);
-
-  // K DMA: instruction c of a page fills LDS bytes [1024c, 1024c + 1024) of
-  // the page slot; the lane's destination chunk (token t, position pos) takes
-  // global chunk pos ^ swizzle(t).
-  auto kdma_off = [&](int sl, int c) __attribute__((always_inline)) -> uint32_t {
-    const int byte = 1024 * c + 16 * lane;
-    const int t = byte / G::KROW;
-    const int pos = (byte % G::KROW) / 16;
-    return (uint32_t)(t * G::KROW + 16 * (pos ^ kswz<D, KVT>(t, sl)));
-  };
-
-  // Page ids: one per lane for the next 64 pages this wave will stream (lane
-  // l <-> wave iteration x = chunk*IPC + l/PPI, slot l%PPI), read back with a
-  // uniform readlane.  Reloading happens once per 64 pages; it is a plain
-  // vector load, so the compiler drains the in-flight DMA there (rare).
-  constexpr int IPC = 64 / G::PPI;  // wave iterations per id chunk
-  bool bad_page = false;
-  int idreg = 0;
-  auto load_ids = [&](int chunk) {
-    const int x = chunk * IPC + lane / G::PPI;
-    const int sl = lane % G::PPI;
-    int pidx = p_begin + G::PPI * (wave + kWaves * x) + sl;
-    if (pidx >= p_end) pidx = p_begin;  // padding slot: any valid page, never unmasked
-    int id = (p_begin < p_end) ? p.block_table[(int64_t)s * p.max_pages + pidx] : 0;
-    const bool bad = (id < 0 || id >= p.num_pages);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) bad_page = true;
-    idreg = bad ? 0 : id;
-  };
-
-  auto issue = [&](int x, int stage) {
-    if (x % IPC == 0) load_ids(x / IPC);
-    int ids[G::PPI];
+  if (is_score) {
+    // ========================= score waves =========================
+    // Q fragments: k-step ks covers dims dim0(ks, g) + [0, 8) for lane group g.
+    h16x8 qf[KSTEPS][NT];
 #pragma unroll
-    for (int sl = 0; sl < G::PPI; ++sl) ids[sl] = __builtin_amdgcn_readlane(idreg, G::PPI * (x % IPC) + sl);
-    const uint32_t st = my_ring + stage * G::STAGE;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int rr = 16 * nt + n16;
 #pragma unroll
-    for (int sl = 0; sl < G::PPI; ++sl) {
-      const char* kp = kbase + (int64_t)ids[sl] * kstride;
-#pragma unroll
-      for (int c = 0; c < G::K_DMA; ++c) dma_saddr(kp, kdma_off(sl, c), st + G::K_OFF + sl * G::KPAGE + 1024 * c);
-      const char* vp = vbase + (int64_t)ids[sl] * vstride;
-#pragma unroll
-      for (int c = 0; c < G::V_DMA; ++c) dma_saddr(vp + 1024 * c, 16 * lane, st + G::V_OFF + sl * G::VPAGE + 1024 * c);
-    }
-    if constexpr (G::Q8) {
-      // [KS slot0 | KS slot1 | VS slot0 | VS slot1], SPAGE bytes each; lane 0
-      // is always active, so the instruction counts once in vmcnt.
-      if (lane < G::S_LANES) {
-        const int byte = 16 * lane;
-        const int region = byte / G::SPAGE;
-        const int off = byte % G::SPAGE;
-        const int sl = region & 1;
-        const int id = sl ? ids[G::PPI - 1] : ids[0];
-        const char* src = (region < 2 ? ksbase : vsbase) + (int64_t)id * sstride + off;
-        dma_vaddr(src, st + G::KS_OFF);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        int dim0;
+        if constexpr (G::Q8) dim0 = 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1);
+        else dim0 = 32 * ks + 8 * g4;
+        qf[ks][nt] = *reinterpret_cast<const h16x8*>(q_lds + rr * D + dim0);
       }
     }
-  };
+    // drafted-row index of each of this lane's rows (for the ancestry mask)
+    int brow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = rowbase + 16 * nt + n16;
+      brow[nt] = (r < M) ? r % B : 0;
+    }
+    __syncthreads();  // Q staging may now be overwritten
+    if constexpr (!L::EARLY) prologue_dma();
 
-  // ---- online softmax state ----
-  f32x4 oacc[MT][NT];
+    float mref[NT], lacc[NT], lt[NT];
+    f32x4 sacc[NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NT], l_run[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-  }
-  const float c2 = p.scale_log2;
+    for (int nt = 0; nt < NT; ++nt) {
+      mref[nt] = -INFINITY;
+      lacc[nt] = 0.f;
+      lt[nt] = 0.f;
+      sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-  constexpr int UT = G::PPI;   // 16-key tiles per wave iteration
-  constexpr int KPL = 4 * UT;  // keys per lane per row tile
+    // Scaled score of accumulator element (nt, i) of the current tile; with
+    // MK, -inf where the key is not visible to the row.
+    int tile_tok0 = 0;
+    bool masked = false;
+    auto zval = [&](int nt, int i, auto mk) __attribute__((always_inline)) -> float {
+      const float z = sacc[nt][i] * c2;
+      if constexpr (!decltype(mk)::value) {
+        return z;
+      } else {
+        const int j = tile_tok0 + 16 * role + 4 * g4 + i;
+        const uint64_t anc = anc_lds[brow[nt]];
+        const uint32_t rel = (uint32_t)(j - base) & 63u;
+        const uint32_t bit = (uint32_t)(anc >> rel) & 1u;
+        const uint32_t vis = (uint32_t)(j < split_end) & ((uint32_t)(j < base) | bit);
+        return vis ? z : -INFINITY;
+      }
+    };
 
-  // Iteration state shared by the phases below.
-  uint32_t st = 0;
-  int tok0 = 0;
-  bool masked = false;
-  float sv[NT][KPL];  // raw scores (masked ones -inf) of the current iteration
-  float tmax[NT];     // their per-row max, log2 units
+    // P = 2^(z - m_ref) -> fp16 into the tile's P buffer; returns the largest
+    // exponent seen (for the overflow test) and leaves the row sums in lt.
+    auto write_p_t = [&](int j, auto mk) __attribute__((always_inline)) -> float {
+      float tmx = -INFINITY;
+      const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float mre = fmaxf(mref[nt], kFiniteFloor);
+        float pv[4];
+        float ls = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float t = zval(nt, i, mk) - mre;
+          tmx = fmaxf(tmx, t);
+          pv[i] = fast_exp2(t);
+          ls += pv[i];
+        }
+        lt[nt] = ls;
+        const h16x4 ph = {(h16)pv[0], (h16)pv[1], (h16)pv[2], (h16)pv[3]};
+        *LDS_PTR(h16x4, pb + ((g4 >> 1) * NT + nt) * 1024 + (n16 + 16 * role) * 16 + 8 * (g4 & 1)) = ph;
+      }
+      return tmx;
+    };
+    auto write_p = [&](int j) __attribute__((always_inline)) -> float {
+      return masked ? write_p_t(j, std::true_type{}) : write_p_t(j, std::false_type{});
+    };
+    // Row maxima of the tile's visible scaled scores (all keys of this page).
+    auto row_max = [&](int nt) __attribute__((always_inline)) -> float {
+      float rm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rm = fmaxf(rm, zval(nt, e, std::true_type{}));
+      return wave_max16(rm);
+    };
 
-  // Phase 1: wait for this iteration's pages, S^T = K Q^T, mask, row max.
-  // Returns true when some row's max passed the lazy-rescale threshold.
-  auto begin_iter = [&](int it) __attribute__((always_inline)) {
-    const int pair = wave + kWaves * it;
-    st = my_ring + (it & 1) * G::STAGE;
-    tok0 = (p_begin + G::PPI * pair) * kPage;
-    masked = (tok0 + G::PPI * kPage) > mask_from;
-  };
-
-  auto phase_scores = [&]() __attribute__((always_inline)) -> bool {
-
-    f32x4 sacc[UT][NT];
+    for (int i = 0; i <= T; ++i) {
+      if (i + R - 1 < T) issue_k(i + R - 1);
+      if (wave == 0 && (i & 15) == 1 && i > 16) {
+        // page ids of chunk (i/16 + 1) into the buffer chunk i/16 - 1 used
+        const int chunk = (i >> 4) + 1;
+        const int off = 64 * chunk + lane;
+        if (off < npg) dma_saddr_b32(bt_row + p_begin + 64 * chunk, 4 * lane, lds0 + L::IDS_OFF + (chunk & 1) * 256);
+      }
+      if (i < T) {
+        const int j = i;
+        tile_tok0 = (p_begin + 4 * j) * kPage;
+        masked = tile_tok0 + 64 > mask_from;
+        const uint32_t st = lds0 + L::KR_OFF + (j % R) * G::K_STAGE;
+        const uint32_t kp = st + role * G::KPAGE + 16 * lane;
 #pragma unroll
-    for (int u = 0; u < UT; ++u)
+        for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (G::Q8) {
+          // this lane's token scales: D/32 fp16 = D/64 dwords; chunk c uses
+          // block 2c + g/2, i.e. half (g/2) of dword c
+          uint32_t sw[D / 64];
+          const uint32_t sp = st + 4 * G::KPAGE + role * D + n16 * (D / 16);
+          if constexpr (D == 256) {
+            const u32x4 t = *LDS_PTR(u32x4, sp);
+            sw[0] = t[0]; sw[1] = t[1]; sw[2] = t[2]; sw[3] = t[3];
+          } else if constexpr (D == 128) {
+            const u32x2 t = *LDS_PTR(u32x2, sp);
+            sw[0] = t[0]; sw[1] = t[1];
+          } else {
+            sw[0] = *LDS_PTR(uint32_t, sp);
+          }
+          const uint32_t sel = (g4 >> 1) ? 0x03020302u : 0x01000100u;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+          for (int c = 0; c < G::KCH; ++c) {
+            const u32x4 raw = *LDS_PTR(u32x4, kp + 1024 * c);
+            const h16x2 d2 = as_h2(__builtin_amdgcn_perm(sw[c], sw[c], sel));
+            const h16x8 k0 = deq8(raw[0], raw[1], d2, d2, d2, d2);
+            const h16x8 k1 = deq8(raw[2], raw[3], d2, d2, d2, d2);
 #pragma unroll
-    for (int u = 0; u < UT; ++u) {
-      if constexpr (KVT == kQ8) {
-        // M row m16 of tile u is key (slot m16/8, token 8*((m16/4)&1) + 4u + m16%4)
-        const int sl = m16 >> 3;
-        const int t = 8 * ((m16 >> 2) & 1) + 4 * u + (m16 & 3);
-        const uint32_t krow = st + G::K_OFF + sl * G::KPAGE + t * G::KROW;
-        const uint32_t srow = st + G::KS_OFF + sl * G::SPAGE + t * (D / 32) * 2;
-        h16 kscale[D / 64];
+            for (int nt = 0; nt < NT; ++nt) {
+              sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * c][nt], sacc[nt], 0, 0, 0);
+              sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * c + 1][nt], sacc[nt], 0, 0, 0);
+            }
+          }
+        } else {
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j) kscale[j] = *LDS_PTR(h16, srow + 2 * (2 * j + (g4 >> 1)));
+          for (int c = 0; c < G::KCH; ++c) {
+            const h16x8 k0 = *LDS_PTR(h16x8, kp + 1024 * c);
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j) {
-          const int c = 4 * j + g4;
-          const u32x4 raw = *LDS_PTR(u32x4, krow + 16 * (c ^ kswz<D, KVT>(t, sl)));
-          const h16x2 d2 = {kscale[j], kscale[j]};
-          h16x2 a0, a1, a2, a3, b0, b1, b2, b3;
-          i8x4_to_h(raw[0], a0, a1);
-          i8x4_to_h(raw[1], a2, a3);
-          i8x4_to_h(raw[2], b0, b1);
-          i8x4_to_h(raw[3], b2, b3);
-          const h16x8 k0 = cat(a0 * d2, a1 * d2, a2 * d2, a3 * d2);
-          const h16x8 k1 = cat(b0 * d2, b1 * d2, b2 * d2, b3 * d2);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[nt][2 * j], sacc[u][nt], 0, 0, 0);
-            sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[nt][2 * j + 1], sacc[u][nt], 0, 0, 0);
+            for (int nt = 0; nt < NT; ++nt)
+              sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[c][nt], sacc[nt], 0, 0, 0);
           }
         }
-      } else {
-        const int t = m16;
-        const uint32_t krow = st + G::K_OFF + t * G::KROW;
+        const float tmx = write_p(j);
+        if (tmx > kLazyRescale) flag_ref(i & 1) = 1;
+      }
+      // K of tile i + 1 must have landed before the barrier
+      if (i + 1 < T) wait_vmcnt_n<NDMA>(min(T - 1, i + R - 1) - (i + 1));
+      lds_barrier();
+      if (flag_set(i & 1)) {
+        // ---- rare path: raise the references (score side) ----
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const int c = 4 * ks + g4;
-          const h16x8 k0 = *LDS_PTR(h16x8, krow + 16 * (c ^ kswz<D, KVT>(t, 0)));
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[nt][ks], sacc[u][nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const float rm = row_max(nt);
+          if (g4 == 0) ex_lds[role * QROWS + 16 * nt + n16] = rm;
         }
-      }
-    }
-
-    // Lane (row m16, group g4) holds, per tile u, accumulator element i = key
-    // (slot g4/2, token 8*(g4&1) + 4u + i) for Q8, or token 4*g4 + i for fp16.
-    bool need = false;
+        lds_barrier();
+        if (wave == 0 && lane == 0) flag_ref(i & 1) = 0;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
+          float nr = mref[nt];
 #pragma unroll
-      for (int u = 0; u < UT; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[nt][4 * u + i] = sacc[u][nt][i];
-      if (masked) {
-        const int r = rowbase + 16 * nt + m16;
-        const uint64_t anc = (r < M) ? anc_lds[r % B] : 0;
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) {
-          int j;
-          if constexpr (KVT == kQ8) j = tok0 + 16 * (g4 >> 1) + 8 * (g4 & 1) + e;
-          else j = tok0 + 4 * g4 + e;
-          // visible iff j < split_end and (j < base or bit (j - base) of anc);
-          // branch-free: 0 <= j - base < 64 always holds when j >= base here.
-          const uint32_t rel = (uint32_t)(j - base) & 63u;
-          const uint32_t bit = (uint32_t)(anc >> rel) & 1u;
-          const uint32_t vis = (uint32_t)(j < split_end) & ((uint32_t)(j < base) | bit);
-          sv[nt][e] = vis ? sv[nt][e] : -INFINITY;
+          for (int q = 0; q < kRoleWaves; ++q) nr = fmaxf(nr, ex_lds[q * QROWS + 16 * nt + n16]);
+          lacc[nt] *= fast_exp2(fmaxf(mref[nt], kFiniteFloor) - fmaxf(nr, kFiniteFloor));
+          mref[nt] = nr;
         }
-      }
-      float mx = sv[nt][0];
+        write_p(i);
 #pragma unroll
-      for (int e = 1; e < KPL; ++e) mx = fmaxf(mx, sv[nt][e]);
-      tmax[nt] = mx * c2;
-      need |= tmax[nt] > m_run[nt] + kLazyRescale;
-    }
-    return __builtin_amdgcn_ballot_w64(need) != 0;
-  };
-
-  // Raise every row's reference max to the largest scaled score seen so far.
-  auto raise_reference = [&]() __attribute__((always_inline)) {
+        for (int nt = 0; nt < NT; ++nt) lacc[nt] += lt[nt];
+        lds_barrier();
+      } else if (i < T) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) m_run[nt] = fmaxf(m_run[nt], wave_max16(tmax[nt]));
-  };
-
-  // Phase 2: P = 2^(t - m_ref) in fp16 (registers only), O^T += V^T P^T.
-  auto phase_pv = [&]() __attribute__((always_inline)) {
-    h16x8 pf[NT];   // Q8: 8 keys per lane (one 32-key k-step)
-    h16x4 pf4[NT];  // fp16: 4 keys per lane (one 16-key k-step)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float mref = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
-      float lsum = 0.f;
-      float pv[KPL];
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        pv[e] = fast_exp2(__builtin_fmaf(sv[nt][e], c2, -mref));
-        lsum += pv[e];
-      }
-      l_run[nt] += lsum;
-      if constexpr (KVT == kQ8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[nt][e] = (h16)pv[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pf4[nt][e] = (h16)pv[e];
+        for (int nt = 0; nt < NT; ++nt) lacc[nt] += lt[nt];
       }
     }
-
-    if constexpr (KVT == kQ8) {
-      const int sl = g4 >> 1;
-      const uint32_t vrow = st + G::V_OFF + sl * G::VPAGE + 8 * (g4 & 1);
-      const uint32_t vsrow = st + G::VS_OFF + sl * G::SPAGE + 16 * (g4 & 1);
-      // This lane's 8 tokens that lie past the split end carry no data (stale
-      // LDS, NaN-poisoned tails): zero their scales so their V reads as 0.
-      u32x4 smask;
-      {
-        const int jt0 = tok0 + 16 * sl + 8 * (g4 & 1);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          smask[e2] = (jt0 + 2 * e2 < split_end ? 0x0000ffffu : 0u) | (jt0 + 2 * e2 + 1 < split_end ? 0xffff0000u : 0u);
-      }
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b) {
-        h16x8 vs = *LDS_PTR(h16x8, vsrow + 32 * b);
-        vs = __builtin_bit_cast(h16x8, __builtin_bit_cast(u32x4, vs) & smask);
-        const h16x2 s01 = {vs[0], vs[1]}, s23 = {vs[2], vs[3]}, s45 = {vs[4], vs[5]}, s67 = {vs[6], vs[7]};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int mt = 2 * b + half;
-          const u32x2 raw = *LDS_PTR(u32x2, vrow + (16 * mt + m16) * 16);
-          h16x2 v01, v23, v45, v67;
-          i8x4_to_h(raw[0], v01, v23);
-          i8x4_to_h(raw[1], v45, v67);
-          const h16x8 vf = cat(v01 * s01, v23 * s23, v45 * s45, v67 * s67);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[nt], oacc[mt][nt], 0, 0, 0);
-        }
-      }
-    } else {
-      const uint32_t vrow = st + G::V_OFF + 8 * g4;
-      u32x2 vmask;
-      {
-        const int jt0 = tok0 + 4 * g4;
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2)
-          vmask[e2] = (jt0 + 2 * e2 < split_end ? 0x0000ffffu : 0u) | (jt0 + 2 * e2 + 1 < split_end ? 0xffff0000u : 0u);
-      }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        h16x4 vf = *LDS_PTR(h16x4, vrow + (16 * mt + m16) * 32);
-        vf = __builtin_bit_cast(h16x4, __builtin_bit_cast(u32x2, vf) & vmask);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, pf4[nt], oacc[mt][nt], 0, 0, 0);
-      }
-    }
-  };
-
-  auto prefetch = [&](int it) __attribute__((always_inline)) {
-    if (it + 1 < n_my) {
-      issue(it + 1, (it + 1) & 1);
-      wait_vmcnt<G::NDMA>();
-    } else {
-      wait_vmcnt<0>();
-    }
-  };
-
-  // P is stored as fp16, so a score may exceed its row's reference max by at
-  // most kLazyRescale (log2 units) before 2^(t - m_ref) leaves the fp16 range.
-  // The reference is fixed while accumulating; if a later page carries a
-  // score beyond that margin (rare: the first page usually sets a max that
-  // holds), the wave raises every row's reference to the largest score seen
-  // so far, clears its accumulators and streams its pages again.  Each such
-  // restart raises some reference by more than the margin, so the number of
-  // restarts is bounded by the score range.
-  if (n_my > 0) issue(0, 0);
-  int it = 0;
-  for (;;) {
-    bool restart = false;
-    for (; it < n_my; ++it) {  // hot loop: nothing here rewrites the accumulators
-      prefetch(it);
-      begin_iter(it);
-      if (phase_scores()) {
-        if (it > 0) {
-          restart = true;
-          break;
-        }
-        raise_reference();  // first page of a pass: nothing accumulated yet
-      }
-      phase_pv();
-    }
-    if (!restart) break;
-    // Rare path: raise the references, clear and stream this wave's pages again.
-    raise_reference();
     wait_vmcnt<0>();
+    if (__builtin_amdgcn_ballot_w64(bad_page) != 0 && lane == 0) flag_ref(2) = 1;
+
+    // ---- epilogue (score side): publish row sums and references ----
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt) {
+      const float l = wave_sum16(lacc[nt]);
+      if (g4 == 0) ex_lds[role * QROWS + 16 * nt + n16] = l;
+    }
+    __syncthreads();
+  } else {
+    // ========================= output waves =========================
+    __syncthreads();  // matches the score waves' Q-fragment barrier
+    if constexpr (!L::EARLY) prologue_dma();
+
+    f32x4 oacc[G::MTO][NT];
+#pragma unroll
+    for (int mt = 0; mt < G::MTO; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) oacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float mref[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) l_run[nt] = 0.f;
-    it = 0;
-    issue(0, 0);
-  }
+    for (int nt = 0; nt < NT; ++nt) mref[nt] = -INFINITY;
 
-  if (bad_page) {
-    poison = true;
-    flagbits |= VA_FLAG_BAD_PAGE;
-  }
-  if (flagbits && lane == 0) atomicOr(p.flags, flagbits);
-
-  // ---- epilogue: merge the 4 waves' states ----
+    for (int i = 0; i <= T; ++i) {
+      if (i + R - 2 < T) issue_v(i + R - 2);
+      if (i >= 1) {
+        const int j = i - 1;
+        const int tile_tok0 = (p_begin + 4 * j) * kPage;
+        const bool vtail = tile_tok0 + 64 > split_end;
+        const uint32_t st = lds0 + L::VR_OFF + (j % R) * G::V_STAGE;
+        const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf;
+        h16x8 pf[2][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) l_run[nt] = wave_sum16(l_run[nt]);
-
-  float2* ml = reinterpret_cast<float2*>(smem + SM::ML_OFF);
-  int* poison_w = reinterpret_cast<int*>(smem + SM::POISON_OFF);
-  __syncthreads();  // every wave is past its ring; LDS may be reused
-  if (g4 == 0) {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) ml[wave * 16 * NT + 16 * nt + m16] = make_float2(m_run[nt], l_run[nt]);
-  }
-  if (lane == 0) poison_w[wave] = poison ? 1 : 0;
-  __syncthreads();
-  bool any_poison = false;
+          for (int nt = 0; nt < NT; ++nt) pf[h][nt] = *LDS_PTR(h16x8, pb + (h * NT + nt) * 1024 + 16 * lane);
+        const int tok_lane = tile_tok0 + 16 * g4;  // this lane's page starts here
+        if constexpr (G::Q8) {
+          // scales of block bb, tokens 8h..8h+7 of page g: one 16-byte read
+          constexpr int NB = (G::DO >= 32) ? G::DO / 32 : 1;  // scale blocks per output wave
+          h16x2 vs[NB][2][4];
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) any_poison |= (poison_w[w] != 0);
-
-  float Mrow[NT], Lrow[NT];
+          for (int b = 0; b < NB; ++b) {
+            const int bb = (role * G::DO) / 32 + b;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float Mx = -INFINITY;
+            for (int h = 0; h < 2; ++h) {
+              u32x4 w = *LDS_PTR(u32x4, st + 4 * G::VPAGE + g4 * D + bb * 32 + 16 * h);
+              if (vtail) w &= tail_mask(tok_lane + 8 * h, split_end);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, ml[w * 16 * NT + 16 * nt + m16].x);
-    float L = 0.f;
+              for (int e = 0; e < 4; ++e) vs[b][h][e] = as_h2(w[e]);
+            }
+          }
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float2 v = ml[w * 16 * NT + 16 * nt + m16];
-      L += (v.x == -INFINITY) ? 0.f : v.y * fast_exp2(v.x - Mx);
-    }
-    Mrow[nt] = Mx;
-    Lrow[nt] = L;
-    const float wown = (m_run[nt] == -INFINITY) ? 0.f : fast_exp2(m_run[nt] - Mx);
+          for (int mt = 0; mt < G::MTO; ++mt) {
+            const int b = (G::DO >= 32) ? (16 * mt) / 32 : 0;
+            const u32x4 raw = *LDS_PTR(u32x4, st + (role * G::VCH + mt) * 1024 + 16 * lane);
+            const h16x8 v0 = deq8(raw[0], raw[1], vs[b][0][0], vs[b][0][1], vs[b][0][2], vs[b][0][3]);
+            const h16x8 v1 = deq8(raw[2], raw[3], vs[b][1][0], vs[b][1][1], vs[b][1][2], vs[b][1][3]);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) oacc[mt][nt] *= wown;
-  }
-
-  // Reduce-scatter over dim quarters: wave w finalises dim tiles [w*MT/4, (w+1)*MT/4).
-  constexpr int QMT = MT / 4;
-  auto epi_slot = [&](int dst, int src) -> int {  // 12 slots: (dst, src != dst)
-    return dst * 3 + (src < dst ? src : src - 1);
-  };
-#pragma unroll
-  for (int dst = 0; dst < kWaves; ++dst) {
-    if (dst == wave) continue;
-    char* region = smem + epi_slot(dst, wave) * SM::QUARTER;
-#pragma unroll
-    for (int qm = 0; qm < QMT; ++qm)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<f32x4*>(region + (qm * NT + nt) * 1024 + 16 * lane) = oacc[dst * QMT + qm][nt];
-  }
-  __syncthreads();
-  f32x4 fin[QMT][NT];
-#pragma unroll
-  for (int qm = 0; qm < QMT; ++qm)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      // own contribution: pick the static slice with a uniform switch
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w)
-        if (w == wave) acc = oacc[w * QMT + qm][nt];
-#pragma unroll
-      for (int src = 0; src < kWaves; ++src) {
-        if (src == wave) continue;
-        const char* region = smem + epi_slot(wave, src) * SM::QUARTER;
-        acc += *reinterpret_cast<const f32x4*>(region + (qm * NT + nt) * 1024 + 16 * lane);
-      }
-      fin[qm][nt] = acc;
-    }
-
-  // ---- write ----
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int r = rowbase + 16 * nt + m16;
-    if (r >= M) continue;
-    const int hl = r / B, b = r % B;
-    const int64_t R = (int64_t)(s * B + b) * p.H + kvh * p.G + hl;
-    const float Mx = Mrow[nt], L = Lrow[nt];
-    if (p.direct) {
-      const float inv = any_poison ? __builtin_nanf("") : 1.0f / L;
-#pragma unroll
-      for (int qm = 0; qm < QMT; ++qm) {
-        const int dim = 16 * (wave * QMT + qm) + 4 * g4;
-        const f32x4 o = fin[qm][nt] * inv;
-        if (p.out_dtype == kF32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + R * D + dim) = o;
-        } else if (p.out_dtype == kF16) {
-          h16x4 h = {(h16)o[0], (h16)o[1], (h16)o[2], (h16)o[3]};
-          *reinterpret_cast<h16x4*>(reinterpret_cast<h16*>(p.out) + R * D + dim) = h;
+            for (int nt = 0; nt < NT; ++nt) {
+              oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v0, pf[0][nt], oacc[mt][nt], 0, 0, 0);
+              oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v1, pf[1][nt], oacc[mt][nt], 0, 0, 0);
+            }
+          }
         } else {
-          u32x2 w;
+          u32x4 tm[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) w[i] = f32_to_bf16_bits(o[2 * i]) | (f32_to_bf16_bits(o[2 * i + 1]) << 16);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + R * D + dim) = w;
+          for (int h = 0; h < 2; ++h) tm[h] = vtail ? tail_mask(tok_lane + 8 * h, split_end) : u32x4{~0u, ~0u, ~0u, ~0u};
+#pragma unroll
+          for (int mt = 0; mt < G::MTO; ++mt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              u32x4 raw = *LDS_PTR(u32x4, st + (role * G::VCH + 2 * mt + h) * 1024 + 16 * lane);
+              raw &= tm[h];
+              const h16x8 vf = __builtin_bit_cast(h16x8, raw);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt)
+                oacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[h][nt], oacc[mt][nt], 0, 0, 0);
+            }
         }
       }
-      if (wave == 0 && g4 == 0 && p.lse)
-        p.lse[R] = any_poison ? __builtin_nanf("") : kLn2 * (Mx + __builtin_log2f(L));
-    } else {
-      float* po = p.part_o + ((int64_t)split * p.nrows + R) * D;
+      // V of tile i must have landed before the barrier
+      if (i < T) wait_vmcnt_n<NDMA>(min(T - 1, i + R - 2) - i);
+      lds_barrier();
+      if (flag_set(i & 1)) {
+        // ---- rare path: raise the references (output side) ----
+        lds_barrier();
 #pragma unroll
-      for (int qm = 0; qm < QMT; ++qm) {
-        const int dim = 16 * (wave * QMT + qm) + 4 * g4;
-        *reinterpret_cast<f32x4*>(po + dim) = any_poison ? f32x4{__builtin_nanf(""), 0.f, 0.f, 0.f} : fin[qm][nt];
+        for (int nt = 0; nt < NT; ++nt) {
+          float nr = mref[nt];
+#pragma unroll
+          for (int q = 0; q < kRoleWaves; ++q) nr = fmaxf(nr, ex_lds[q * QROWS + 16 * nt + n16]);
+          const float alpha = fast_exp2(fmaxf(mref[nt], kFiniteFloor) - fmaxf(nr, kFiniteFloor));
+#pragma unroll
+          for (int mt = 0; mt < G::MTO; ++mt) oacc[mt][nt] *= alpha;
+          mref[nt] = nr;
+        }
+        lds_barrier();
       }
-      if (wave == 0 && g4 == 0) {
-        p.part_m[(int64_t)split * p.nrows + R] = any_poison ? 0.f : Mx;
-        p.part_l[(int64_t)split * p.nrows + R] = any_poison ? __builtin_nanf("") : L;
+    }
+    wait_vmcnt<0>();
+    if (__builtin_amdgcn_ballot_w64(bad_page) != 0 && lane == 0) flag_ref(2) = 1;
+    __syncthreads();  // the score waves' row sums are in ex_lds
+
+    // ---- epilogue (output side): normalise or write partials ----
+    const bool any_poison = poison || flag_set(2);
+    const int dq = role;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = rowbase + 16 * nt + n16;
+      if (r >= M) continue;
+      float Lrow = 0.f;
+#pragma unroll
+      for (int q = 0; q < kRoleWaves; ++q) Lrow += ex_lds[q * QROWS + 16 * nt + n16];
+      const int hl = r / B, b = r % B;
+      const int64_t Rg = (int64_t)(s * B + b) * p.H + kvh * p.G + hl;
+      if (p.direct) {
+        const float inv = any_poison ? __builtin_nanf("") : 1.0f / Lrow;
+#pragma unroll
+        for (int mt = 0; mt < G::MTO; ++mt) {
+          const int dim = dq * G::DO + 16 * mt + 4 * g4;
+          const f32x4 o = oacc[mt][nt] * inv;
+          if (p.out_dtype == kF32) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + Rg * D + dim) = o;
+          } else if (p.out_dtype == kF16) {
+            const h16x4 h = {(h16)o[0], (h16)o[1], (h16)o[2], (h16)o[3]};
+            *reinterpret_cast<h16x4*>(reinterpret_cast<h16*>(p.out) + Rg * D + dim) = h;
+          } else {
+            u32x2 w;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) w[e] = f32_to_bf16_bits(o[2 * e]) | (f32_to_bf16_bits(o[2 * e + 1]) << 16);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + Rg * D + dim) = w;
+          }
+        }
+        if (dq == 0 && g4 == 0 && p.lse)
+          p.lse[Rg] = any_poison ? __builtin_nanf("") : kLn2 * (mref[nt] + __builtin_log2f(Lrow));
+      } else {
+        float* po = p.part_o + ((int64_t)split * p.nrows + Rg) * D;
+#pragma unroll
+        for (int mt = 0; mt < G::MTO; ++mt) {
+          const int dim = dq * G::DO + 16 * mt + 4 * g4;
+          *reinterpret_cast<f32x4*>(po + dim) = any_poison ? f32x4{__builtin_nanf(""), 0.f, 0.f, 0.f} : oacc[mt][nt];
+        }
+        if (dq == 0 && g4 == 0) {
+          p.part_m[(int64_t)split * p.nrows + Rg] = any_poison ? 0.f : mref[nt];
+          p.part_l[(int64_t)split * p.nrows + Rg] = any_poison ? __builtin_nanf("") : Lrow;
+        }
       }
+    }
+    if (wave == kRoleWaves && lane == 0) {
+      const uint32_t bits = flagbits | (flag_set(2) ? (uint32_t)VA_FLAG_BAD_PAGE : 0u);
+      if (bits) atomicOr(p.flags, bits);
     }
   }
 }
@@ -784,7 +819,7 @@ bool partial_supported(int D, int kv_dtype, int nt) {
 template <int D, int KVT, int NT>
 static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.S * p.row_groups), (unsigned)p.KVH, (unsigned)p.num_seqs);
-  hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT>), grid, dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
 }
 
