@@ -11,8 +11,6 @@
 namespace va {
 
 constexpr int kPage = 16;
-constexpr int kWaves = 4;            // waves per workgroup of the partial kernel
-constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxRows = 64;         // B limit (ancestry bitmask width)
 constexpr size_t kHeaderBytes = 256; // workspace flag header
@@ -59,7 +57,7 @@ struct MergeParams {
 
 // Tiling the plan picks for the partial kernel.
 struct Tiling {
-  int nt;          // 16-row MFMA tiles per workgroup (1, 2, 3, 4 or 6)
+  int nt;          // 16-row MFMA tiles per workgroup (2, 4 or 6)
   int row_groups;  // ceil(B*G / (16*nt))
 };
 

@@ -168,26 +168,34 @@ template <int D, int KVT, int NT>
 struct Lay {
   using G = Geo<D, KVT>;
   static constexpr int P_BUF = 2 * NT * 1024;  // one tile's P: [h][nt][lane] x 16 B
-  static constexpr int MISC = 512 + 512 + 4 * 16 * NT * 4 + 16;
+  static constexpr int EX_BYTES = 2 * 16 * NT * 4;
+  static constexpr int MISC = 512 + 512 + EX_BYTES + 16;
   static constexpr int BUDGET = 160 * 1024;
-  static constexpr int PAIR = G::K_STAGE + G::V_STAGE;
-  static constexpr int R = (4 * PAIR + 2 * P_BUF + MISC <= BUDGET) ? 4 : (3 * PAIR + 2 * P_BUF + MISC <= BUDGET) ? 3 : 2;
+  static constexpr int AVAIL = BUDGET - 2 * P_BUF - MISC;
+  // deepest K / V rings that fit (V is consumed one iteration after K)
+  static constexpr int pick() {
+    constexpr int c[5][2] = {{4, 4}, {3, 4}, {3, 3}, {2, 3}, {2, 2}};
+    for (int i = 0; i < 5; ++i)
+      if (c[i][0] * G::K_STAGE + c[i][1] * G::V_STAGE <= AVAIL) return i;
+    return 4;
+  }
+  static constexpr int RK = pick() == 0 ? 4 : pick() <= 2 ? 3 : 2;
+  static constexpr int RV = pick() <= 1 ? 4 : pick() <= 3 ? 3 : 2;
   static constexpr int KR_OFF = 0;
-  static constexpr int VR_OFF = R * G::K_STAGE;
-  static constexpr int P_OFF = VR_OFF + R * G::V_STAGE;
+  static constexpr int VR_OFF = RK * G::K_STAGE;
+  static constexpr int P_OFF = VR_OFF + RV * G::V_STAGE;
   static constexpr int IDS_OFF = P_OFF + 2 * P_BUF;  // int32 [2][64] page ids
   static constexpr int ANC_OFF = IDS_OFF + 512;      // uint64 [64] ancestry masks
-  static constexpr int EX_OFF = ANC_OFF + 512;       // float [4][16 NT] row exchange
-  static constexpr int FLAG_OFF = EX_OFF + 4 * 16 * NT * 4;  // int flags [3]
+  static constexpr int EX_OFF = ANC_OFF + 512;       // float [2][16 NT] row exchange
+  static constexpr int FLAG_OFF = EX_OFF + EX_BYTES; // int flags [3]
   static constexpr int BYTES = FLAG_OFF + 16;
-  // Q staging (fp16 [16 NT][D]) during the prologue: V stages R-2 and R-1
-  // receive nothing before the first iteration, so the first K/V pages can
-  // already be in flight while Q is converted; otherwise the ring start.
+  // Q staging (fp16 [16 NT][D]) during the prologue: the V ring receives
+  // nothing before the first iteration.
   static constexpr int QST_BYTES = 16 * NT * D * 2;
-  static constexpr bool EARLY = QST_BYTES <= 2 * G::V_STAGE;
-  static constexpr int QST_OFF = EARLY ? VR_OFF + (R - 2) * G::V_STAGE : 0;
+  static constexpr int QST_OFF = VR_OFF;
   static_assert(BYTES <= BUDGET, "LDS budget");
-  static_assert(EARLY || QST_BYTES <= P_OFF, "Q staging fits the rings");
+  static_assert(QST_BYTES <= RV * G::V_STAGE, "Q staging fits the V ring");
+  static_assert(RK >= 2 && RV >= 2, "ring depth");
 };
 
 // ---- numeric helpers ---------------------------------------------------------
@@ -216,31 +224,6 @@ __device__ __forceinline__ h16x8 deq8(uint32_t w0, uint32_t w1, h16x2 s0, h16x2 
   i8x4_to_h(w0, a, b);
   i8x4_to_h(w1, c, d);
   return cat(a * s0, b * s1, c * s2, d * s3);
-}
-
-__device__ __forceinline__ h16x8 load_q8(const void* q, int dtype, int64_t elem) {
-  if (dtype == kBF16) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(q) + elem);
-    h16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[2 * i] = (h16)__builtin_bit_cast(float, raw[i] << 16);
-      r[2 * i + 1] = (h16)__builtin_bit_cast(float, raw[i] & 0xffff0000u);
-    }
-    return r;
-  } else if (dtype == kF16) {
-    return *reinterpret_cast<const h16x8*>(reinterpret_cast<const h16*>(q) + elem);
-  } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + elem);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(q) + elem + 4);
-    h16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r[i] = (h16)a[i];
-      r[4 + i] = (h16)b[i];
-    }
-    return r;
-  }
 }
 
 __device__ __forceinline__ float wave_max16(float x) {  // max over lanes l, l^16, l^32, l^48
@@ -278,7 +261,9 @@ template <int D, int KVT, int NT>
 __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const PartialParams p) {
   using G = Geo<D, KVT>;
   using L = Lay<D, KVT, NT>;
-  constexpr int R = L::R;
+  static_assert(NT % 2 == 0, "the score waves take half the rows each");
+  constexpr int RK = L::RK, RV = L::RV;
+  constexpr int NS = NT / 2;  // row tiles per score wave
   constexpr int KSTEPS = G::KSTEPS;
   constexpr int NDMA = G::NDMA;
   constexpr int QROWS = 16 * NT;
@@ -311,8 +296,41 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   const int M = B * p.G;
   const int rowbase = rg * QROWS;
 
-  // ---- validate sequence metadata (device-resident) ----
+  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_pages;
+
+  // ---- prologue loads, all in flight together ----
+  // (1) ctx; (2) the block-table entries of this split as placed for
+  // ctx = max_ctx (the usual case; checked below, reloaded otherwise);
+  // (3) the group's Q rows as raw 16-byte units; (4) the parent array.
   int ctx = p.ctx_lens[s];
+  const int npg_max = (p.max_ctx + kPage - 1) / kPage;
+  const int pps_spec = (npg_max + p.S - 1) / p.S;
+  const int pb_spec = min(split * pps_spec, npg_max);
+  const int pe_spec = min(pb_spec + pps_spec, npg_max);
+  int id_spec = 0;
+  if (tid < 128 && pb_spec + tid < pe_spec) id_spec = bt_row[pb_spec + tid];
+
+  const bool qf32 = p.q_dtype == kF32;
+  const int upr = qf32 ? D / 4 : D / 8;  // 16-byte Q units per row
+  constexpr int QU_MAX = (QROWS * (D / 4) + kBlockThreads - 1) / kBlockThreads;
+  u32x4 qraw[QU_MAX];
+#pragma unroll
+  for (int u = 0; u < QU_MAX; ++u) {
+    qraw[u] = u32x4{0u, 0u, 0u, 0u};
+    const int idx = tid + u * kBlockThreads;
+    const int rr = idx / upr, c = idx % upr;
+    const int r = rowbase + rr;
+    if (rr < QROWS && r < M) {
+      const int hl = r / B, b = r % B;
+      const int64_t qrow = ((int64_t)(s * B + b) * p.H + kvh * p.G + hl) * D;
+      const char* src = reinterpret_cast<const char*>(p.q) + (qrow + (int64_t)c * (qf32 ? 4 : 8)) * (qf32 ? 4 : 2);
+      qraw[u] = *reinterpret_cast<const u32x4*>(src);
+    }
+  }
+  int par = 0;
+  if (p.parent && lane < B) par = p.parent[(int64_t)s * B + lane];
+
+  // ---- validate sequence metadata (device-resident) ----
   bool poison = false;
   if (ctx < B || ctx > p.max_ctx || ctx > p.max_pages * kPage) {
     poison = true;
@@ -320,15 +338,13 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   }
   uint32_t flagbits = poison ? VA_FLAG_BAD_CTX : 0u;
   if (p.parent) {
-    bool bad = false;
-    if (lane < B) {
-      const int par = p.parent[(int64_t)s * B + lane];
-      bad = (par < -1 || par >= lane);
-    }
+    const bool bad = lane < B && (par < -1 || par >= lane);
     if (__builtin_amdgcn_ballot_w64(bad) != 0) {
       poison = true;
       flagbits |= VA_FLAG_BAD_PARENT;
     }
+  } else {
+    par = lane - 1;
   }
   const int base = ctx - B;  // slot of drafted row 0
 
@@ -341,7 +357,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   const int T = (npg + 3) >> 2;
   const int split_end = min(ctx, p_end * kPage);
   const int mask_from = min(base, split_end);  // first token that needs a per-key test
-  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_pages;
 
   int* ids_lds = reinterpret_cast<int*>(smem + L::IDS_OFF);
   uint64_t* anc_lds = reinterpret_cast<uint64_t*>(smem + L::ANC_OFF);
@@ -357,22 +372,58 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     return __builtin_amdgcn_readfirstlane(flag_ref(idx)) != 0;
   };
 
-  // ---- prologue 1: page ids of the first 128 pages, ancestry masks ----
-  if (tid < 128) ids_lds[tid] = (tid < npg) ? bt_row[p_begin + tid] : 0;
-  if (tid < B) {
-    uint64_t a = 0;
-    int i = tid;
-    for (int guard = 0; guard < kMaxRows && i >= 0; ++guard) {
-      a |= (uint64_t)1 << i;
-      const int par = p.parent ? p.parent[(int64_t)s * B + i] : i - 1;
-      i = (par < i) ? par : -1;  // a malformed parent is flagged above; stop the walk
+  // ---- prologue stores: page ids of the first 128 pages, ancestry, Q ----
+  if (tid < 128) {
+    const bool spec_ok = (p_begin == pb_spec) && (npg <= pe_spec - pb_spec);
+    ids_lds[tid] = (tid < npg) ? (spec_ok ? id_spec : bt_row[p_begin + tid]) : 0;
+  }
+  if (wave == 0) {
+    // anc(i) = {i} + anc(parent[i]) by pointer jumping: after k rounds, a
+    // holds the ancestors within distance 2^k and pr the one at distance 2^k.
+    int pr = (lane < B && par < lane) ? par : -1;
+    uint64_t a = (lane < B) ? (uint64_t)1 << lane : 0;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+      const int src = pr < 0 ? lane : pr;
+      const uint64_t pa = __shfl(a, src);
+      const int pp = __shfl(pr, src);
+      if (pr >= 0) {
+        a |= pa;
+        pr = pp;
+      }
     }
-    anc_lds[tid] = poison ? 0 : a;
+    if (lane < B) anc_lds[lane] = poison ? 0 : a;
   }
   if (tid == 0) {
     flag_ref(0) = 0;
     flag_ref(1) = 0;
     flag_ref(2) = 0;
+  }
+  h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
+#pragma unroll
+  for (int u = 0; u < QU_MAX; ++u) {
+    const int idx = tid + u * kBlockThreads;
+    const int rr = idx / upr, c = idx % upr;
+    if (rr < QROWS) {
+      const u32x4 w = qraw[u];
+      if (qf32) {
+        const f32x4 x = __builtin_bit_cast(f32x4, w);
+        h16x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = (h16)x[e];
+        *reinterpret_cast<h16x4*>(q_lds + rr * D + 4 * c) = h;
+      } else if (p.q_dtype == kBF16) {
+        h16x8 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[2 * e] = (h16)__builtin_bit_cast(float, w[e] << 16);
+          h[2 * e + 1] = (h16)__builtin_bit_cast(float, w[e] & 0xffff0000u);
+        }
+        *reinterpret_cast<h16x8*>(q_lds + rr * D + 8 * c) = h;
+      } else {
+        *reinterpret_cast<u32x4*>(q_lds + rr * D + 8 * c) = w;
+      }
+    }
   }
   __syncthreads();
 
@@ -398,11 +449,11 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     return id;
   };
 
-  // Score wave p: K page p of tile j (4 KB chunks; lane (g, m) of chunk c
+  // Score wave w: K page w of tile j (1 KB chunks; lane (g, m) of chunk c
   // carries token m, bytes [64c + 16g, 64c + 16g + 16)), plus its scales.
   auto issue_k = [&](int j) __attribute__((always_inline)) {
     const int id = __builtin_amdgcn_readfirstlane(page_id(4 * j + role));
-    const uint32_t st = lds0 + L::KR_OFF + (j % R) * G::K_STAGE;
+    const uint32_t st = lds0 + L::KR_OFF + (j % RK) * G::K_STAGE;
     const char* src = kbase + (int64_t)id * kstride;
     const uint32_t voff = n16 * G::KROW + 16 * g4;
 #pragma unroll
@@ -417,7 +468,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // [16hh, 16hh + 16) of its 16-token row), plus page q's V scales.
   auto issue_v = [&](int j) __attribute__((always_inline)) {
     const int id = page_id(4 * j + g4);
-    const uint32_t st = lds0 + L::VR_OFF + (j % R) * G::V_STAGE;
+    const uint32_t st = lds0 + L::VR_OFF + (j % RV) * G::V_STAGE;
     const char* src = vbase + (int64_t)id * vstride + (int64_t)(role * G::DO + n16) * G::VROW;
 #pragma unroll
     for (int mt = 0; mt < G::MTO; ++mt)
@@ -430,48 +481,24 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     }
   };
 
-  auto prologue_dma = [&]() __attribute__((always_inline)) {
-    if (is_score) {
-#pragma unroll
-      for (int j = 0; j < R - 1; ++j)
-        if (j < T) issue_k(j);
-    } else {
-#pragma unroll
-      for (int j = 0; j < R - 2; ++j)
-        if (j < T) issue_v(j);
-    }
-  };
-
-  if constexpr (L::EARLY) prologue_dma();
-
-  // ---- prologue 2: Q rows of this group as fp16 through LDS ----
-  h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
-  {
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < QROWS * CH; idx += kBlockThreads) {
-      const int rr = idx / CH, c8 = idx % CH;
-      const int r = rowbase + rr;
-      h16x8 v = h16x8{};
-      if (r < M) {
-        const int hl = r / B, b = r % B;
-        const int64_t qrow = ((int64_t)(s * B + b) * p.H + kvh * p.G + hl) * D;
-        v = load_q8(p.q, p.q_dtype, qrow + 8 * c8);
-      }
-      *reinterpret_cast<h16x8*>(q_lds + rr * D + 8 * c8) = v;
-    }
-  }
-  __syncthreads();
-
   const float c2 = p.scale_log2;
-  const int fbuf = L::P_BUF;  // bytes of one P buffer
+  constexpr int fbuf = L::P_BUF;  // bytes of one P buffer
 
   if (is_score) {
     // ========================= score waves =========================
-    // Q fragments: k-step ks covers dims dim0(ks, g) + [0, 8) for lane group g.
-    h16x8 qf[KSTEPS][NT];
+    // wave (rh, kh): rows [16 NS rh, 16 NS (rh + 1)) of the group, pages
+    // 2kh and 2kh + 1 of every tile.
+    const int rh = role & 1, kh = role >> 1;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int rr = 16 * nt + n16;
+    for (int j = 0; j < RK - 1; ++j)
+      if (j < T) issue_k(j);
+
+    // Q fragments: k-step ks covers dims dim0(ks, g) + [0, 8) for lane group g.
+    h16x8 qf[KSTEPS][NS];
+    int brow[NS];  // drafted-row index of each of this lane's rows (ancestry mask)
+#pragma unroll
+    for (int nt = 0; nt < NS; ++nt) {
+      const int rr = 16 * (NS * rh + nt) + n16;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         int dim0;
@@ -479,37 +506,34 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         else dim0 = 32 * ks + 8 * g4;
         qf[ks][nt] = *reinterpret_cast<const h16x8*>(q_lds + rr * D + dim0);
       }
-    }
-    // drafted-row index of each of this lane's rows (for the ancestry mask)
-    int brow[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int r = rowbase + 16 * nt + n16;
+      const int r = rowbase + rr;
       brow[nt] = (r < M) ? r % B : 0;
     }
-    __syncthreads();  // Q staging may now be overwritten
-    if constexpr (!L::EARLY) prologue_dma();
+    // tile 0's K (R_K - 2 more tiles queued behind it) must have landed and
+    // be visible to the partner wave before the first iteration
+    if (T > 0) wait_vmcnt_n<NDMA>(min(T, RK - 1) - 1);
+    __syncthreads();
 
-    float mref[NT], lacc[NT], lt[NT];
-    f32x4 sacc[NT];
+    float mref[NS], lacc[NS], lt[NS];
+    f32x4 sacc[2][NS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NS; ++nt) {
       mref[nt] = -INFINITY;
       lacc[nt] = 0.f;
       lt[nt] = 0.f;
-      sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[0][nt] = sacc[1][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Scaled score of accumulator element (nt, i) of the current tile; with
-    // MK, -inf where the key is not visible to the row.
+    // Scaled score of accumulator element (u, nt, i) of the current tile;
+    // with MK, -inf where the key is not visible to the row.
     int tile_tok0 = 0;
     bool masked = false;
-    auto zval = [&](int nt, int i, auto mk) __attribute__((always_inline)) -> float {
-      const float z = sacc[nt][i] * c2;
+    auto zval = [&](int u, int nt, int i, auto mk) __attribute__((always_inline)) -> float {
+      const float z = sacc[u][nt][i] * c2;
       if constexpr (!decltype(mk)::value) {
         return z;
       } else {
-        const int j = tile_tok0 + 16 * role + 4 * g4 + i;
+        const int j = tile_tok0 + 16 * (2 * kh + u) + 4 * g4 + i;
         const uint64_t anc = anc_lds[brow[nt]];
         const uint32_t rel = (uint32_t)(j - base) & 63u;
         const uint32_t bit = (uint32_t)(anc >> rel) & 1u;
@@ -522,38 +546,45 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     // exponent seen (for the overflow test) and leaves the row sums in lt.
     auto write_p_t = [&](int j, auto mk) __attribute__((always_inline)) -> float {
       float tmx = -INFINITY;
-      const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf;
+      const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf + (g4 >> 1) * NT * 1024 + 8 * (g4 & 1);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < NS; ++nt) {
         const float mre = fmaxf(mref[nt], kFiniteFloor);
-        float pv[4];
         float ls = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float t = zval(nt, i, mk) - mre;
-          tmx = fmaxf(tmx, t);
-          pv[i] = fast_exp2(t);
-          ls += pv[i];
+        for (int u = 0; u < 2; ++u) {
+          float pv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float t;
+            if constexpr (decltype(mk)::value) t = zval(u, nt, i, mk) - mre;
+            else t = __builtin_fmaf(sacc[u][nt][i], c2, -mre);
+            tmx = fmaxf(tmx, t);
+            pv[i] = fast_exp2(t);
+            ls += pv[i];
+          }
+          const h16x4 ph = {(h16)pv[0], (h16)pv[1], (h16)pv[2], (h16)pv[3]};
+          *LDS_PTR(h16x4, pb + (NS * rh + nt) * 1024 + (n16 + 16 * (2 * kh + u)) * 16) = ph;
         }
         lt[nt] = ls;
-        const h16x4 ph = {(h16)pv[0], (h16)pv[1], (h16)pv[2], (h16)pv[3]};
-        *LDS_PTR(h16x4, pb + ((g4 >> 1) * NT + nt) * 1024 + (n16 + 16 * role) * 16 + 8 * (g4 & 1)) = ph;
       }
       return tmx;
     };
     auto write_p = [&](int j) __attribute__((always_inline)) -> float {
       return masked ? write_p_t(j, std::true_type{}) : write_p_t(j, std::false_type{});
     };
-    // Row maxima of the tile's visible scaled scores (all keys of this page).
+    // Row maxima of the tile's visible scaled scores over this wave's pages.
     auto row_max = [&](int nt) __attribute__((always_inline)) -> float {
       float rm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rm = fmaxf(rm, zval(nt, e, std::true_type{}));
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rm = fmaxf(rm, zval(u, nt, e, std::true_type{}));
       return wave_max16(rm);
     };
 
     for (int i = 0; i <= T; ++i) {
-      if (i + R - 1 < T) issue_k(i + R - 1);
+      if (i + RK - 1 < T) issue_k(i + RK - 1);
       if (wave == 0 && (i & 15) == 1 && i > 16) {
         // page ids of chunk (i/16 + 1) into the buffer chunk i/16 - 1 used
         const int chunk = (i >> 4) + 1;
@@ -564,92 +595,100 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         const int j = i;
         tile_tok0 = (p_begin + 4 * j) * kPage;
         masked = tile_tok0 + 64 > mask_from;
-        const uint32_t st = lds0 + L::KR_OFF + (j % R) * G::K_STAGE;
-        const uint32_t kp = st + role * G::KPAGE + 16 * lane;
+        const uint32_t st = lds0 + L::KR_OFF + (j % RK) * G::K_STAGE;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int nt = 0; nt < NS; ++nt) sacc[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (G::Q8) {
-          // this lane's token scales: D/32 fp16 = D/64 dwords; chunk c uses
-          // block 2c + g/2, i.e. half (g/2) of dword c
-          uint32_t sw[D / 64];
-          const uint32_t sp = st + 4 * G::KPAGE + role * D + n16 * (D / 16);
-          if constexpr (D == 256) {
-            const u32x4 t = *LDS_PTR(u32x4, sp);
-            sw[0] = t[0]; sw[1] = t[1]; sw[2] = t[2]; sw[3] = t[3];
-          } else if constexpr (D == 128) {
-            const u32x2 t = *LDS_PTR(u32x2, sp);
-            sw[0] = t[0]; sw[1] = t[1];
-          } else {
-            sw[0] = *LDS_PTR(uint32_t, sp);
+          // per page: this lane's token scales, D/32 fp16 = D/64 dwords;
+          // chunk c uses block 2c + g/2, i.e. half (g/2) of dword c
+          uint32_t sw[2][D / 64];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const uint32_t sp = st + 4 * G::KPAGE + (2 * kh + u) * D + n16 * (D / 16);
+            if constexpr (D == 256) {
+              const u32x4 t = *LDS_PTR(u32x4, sp);
+              sw[u][0] = t[0]; sw[u][1] = t[1]; sw[u][2] = t[2]; sw[u][3] = t[3];
+            } else if constexpr (D == 128) {
+              const u32x2 t = *LDS_PTR(u32x2, sp);
+              sw[u][0] = t[0]; sw[u][1] = t[1];
+            } else {
+              sw[u][0] = *LDS_PTR(uint32_t, sp);
+            }
           }
           const uint32_t sel = (g4 >> 1) ? 0x03020302u : 0x01000100u;
 #pragma unroll
           for (int c = 0; c < G::KCH; ++c) {
-            const u32x4 raw = *LDS_PTR(u32x4, kp + 1024 * c);
-            const h16x2 d2 = as_h2(__builtin_amdgcn_perm(sw[c], sw[c], sel));
-            const h16x8 k0 = deq8(raw[0], raw[1], d2, d2, d2, d2);
-            const h16x8 k1 = deq8(raw[2], raw[3], d2, d2, d2, d2);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * c][nt], sacc[nt], 0, 0, 0);
-              sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * c + 1][nt], sacc[nt], 0, 0, 0);
+            for (int u = 0; u < 2; ++u) {
+              const u32x4 raw = *LDS_PTR(u32x4, st + (2 * kh + u) * G::KPAGE + 1024 * c + 16 * lane);
+              const h16x2 d2 = as_h2(__builtin_amdgcn_perm(sw[u][c], sw[u][c], sel));
+              const h16x8 k0 = deq8(raw[0], raw[1], d2, d2, d2, d2);
+              const h16x8 k1 = deq8(raw[2], raw[3], d2, d2, d2, d2);
+#pragma unroll
+              for (int nt = 0; nt < NS; ++nt) {
+                sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * c][nt], sacc[u][nt], 0, 0, 0);
+                sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * c + 1][nt], sacc[u][nt], 0, 0, 0);
+              }
             }
           }
         } else {
 #pragma unroll
           for (int c = 0; c < G::KCH; ++c) {
-            const h16x8 k0 = *LDS_PTR(h16x8, kp + 1024 * c);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              sacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[c][nt], sacc[nt], 0, 0, 0);
+            for (int u = 0; u < 2; ++u) {
+              const h16x8 k0 = *LDS_PTR(h16x8, st + (2 * kh + u) * G::KPAGE + 1024 * c + 16 * lane);
+#pragma unroll
+              for (int nt = 0; nt < NS; ++nt)
+                sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[c][nt], sacc[u][nt], 0, 0, 0);
+            }
           }
         }
         const float tmx = write_p(j);
         if (tmx > kLazyRescale) flag_ref(i & 1) = 1;
       }
-      // K of tile i + 1 must have landed before the barrier
-      if (i + 1 < T) wait_vmcnt_n<NDMA>(min(T - 1, i + R - 1) - (i + 1));
+      // K of tile i + 1 (partly the partner wave's) must have landed before the barrier
+      if (i + 1 < T) wait_vmcnt_n<NDMA>(min(T - 1, i + RK - 1) - (i + 1));
       lds_barrier();
       if (flag_set(i & 1)) {
         // ---- rare path: raise the references (score side) ----
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
+        for (int nt = 0; nt < NS; ++nt) {
           const float rm = row_max(nt);
-          if (g4 == 0) ex_lds[role * QROWS + 16 * nt + n16] = rm;
+          if (g4 == 0) ex_lds[kh * QROWS + 16 * (NS * rh + nt) + n16] = rm;
         }
         lds_barrier();
         if (wave == 0 && lane == 0) flag_ref(i & 1) = 0;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float nr = mref[nt];
-#pragma unroll
-          for (int q = 0; q < kRoleWaves; ++q) nr = fmaxf(nr, ex_lds[q * QROWS + 16 * nt + n16]);
+        for (int nt = 0; nt < NS; ++nt) {
+          const int row = 16 * (NS * rh + nt) + n16;
+          const float nr = fmaxf(mref[nt], fmaxf(ex_lds[row], ex_lds[QROWS + row]));
           lacc[nt] *= fast_exp2(fmaxf(mref[nt], kFiniteFloor) - fmaxf(nr, kFiniteFloor));
           mref[nt] = nr;
         }
         write_p(i);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) lacc[nt] += lt[nt];
+        for (int nt = 0; nt < NS; ++nt) lacc[nt] += lt[nt];
         lds_barrier();
       } else if (i < T) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) lacc[nt] += lt[nt];
+        for (int nt = 0; nt < NS; ++nt) lacc[nt] += lt[nt];
       }
     }
     wait_vmcnt<0>();
     if (__builtin_amdgcn_ballot_w64(bad_page) != 0 && lane == 0) flag_ref(2) = 1;
 
-    // ---- epilogue (score side): publish row sums and references ----
+    // ---- epilogue (score side): publish the row sums over this wave's keys ----
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NS; ++nt) {
       const float l = wave_sum16(lacc[nt]);
-      if (g4 == 0) ex_lds[role * QROWS + 16 * nt + n16] = l;
+      if (g4 == 0) ex_lds[kh * QROWS + 16 * (NS * rh + nt) + n16] = l;
     }
     __syncthreads();
   } else {
     // ========================= output waves =========================
     __syncthreads();  // matches the score waves' Q-fragment barrier
-    if constexpr (!L::EARLY) prologue_dma();
 
     f32x4 oacc[G::MTO][NT];
 #pragma unroll
@@ -661,12 +700,19 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     for (int nt = 0; nt < NT; ++nt) mref[nt] = -INFINITY;
 
     for (int i = 0; i <= T; ++i) {
-      if (i + R - 2 < T) issue_v(i + R - 2);
+      if (i == 0) {
+        // the V ring held the Q staging until the barrier above
+#pragma unroll
+        for (int j = 0; j < RV - 1; ++j)
+          if (j < T) issue_v(j);
+      } else if (i + RV - 2 < T) {
+        issue_v(i + RV - 2);
+      }
       if (i >= 1) {
         const int j = i - 1;
         const int tile_tok0 = (p_begin + 4 * j) * kPage;
         const bool vtail = tile_tok0 + 64 > split_end;
-        const uint32_t st = lds0 + L::VR_OFF + (j % R) * G::V_STAGE;
+        const uint32_t st = lds0 + L::VR_OFF + (j % RV) * G::V_STAGE;
         const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf;
         h16x8 pf[2][NT];
 #pragma unroll
@@ -719,16 +765,15 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         }
       }
       // V of tile i must have landed before the barrier
-      if (i < T) wait_vmcnt_n<NDMA>(min(T - 1, i + R - 2) - i);
+      if (i < T) wait_vmcnt_n<NDMA>(min(T - 1, i + RV - 2) - i);
       lds_barrier();
       if (flag_set(i & 1)) {
         // ---- rare path: raise the references (output side) ----
         lds_barrier();
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          float nr = mref[nt];
-#pragma unroll
-          for (int q = 0; q < kRoleWaves; ++q) nr = fmaxf(nr, ex_lds[q * QROWS + 16 * nt + n16]);
+          const int row = 16 * nt + n16;
+          const float nr = fmaxf(mref[nt], fmaxf(ex_lds[row], ex_lds[QROWS + row]));
           const float alpha = fast_exp2(fmaxf(mref[nt], kFiniteFloor) - fmaxf(nr, kFiniteFloor));
 #pragma unroll
           for (int mt = 0; mt < G::MTO; ++mt) oacc[mt][nt] *= alpha;
@@ -748,9 +793,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     for (int nt = 0; nt < NT; ++nt) {
       const int r = rowbase + 16 * nt + n16;
       if (r >= M) continue;
-      float Lrow = 0.f;
-#pragma unroll
-      for (int q = 0; q < kRoleWaves; ++q) Lrow += ex_lds[q * QROWS + 16 * nt + n16];
+      const float Lrow = ex_lds[16 * nt + n16] + ex_lds[QROWS + 16 * nt + n16];
       const int hl = r / B, b = r % B;
       const int64_t Rg = (int64_t)(s * B + b) * p.H + kvh * p.G + hl;
       if (p.direct) {
@@ -762,7 +805,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
           if (p.out_dtype == kF32) {
             *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + Rg * D + dim) = o;
           } else if (p.out_dtype == kF16) {
-            const h16x4 h = {(h16)o[0], (h16)o[1], (h16)o[2], (h16)o[3]};
+            h16x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = (h16)o[e];
             *reinterpret_cast<h16x4*>(reinterpret_cast<h16*>(p.out) + Rg * D + dim) = h;
           } else {
             u32x2 w;
@@ -798,22 +843,20 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
 // ---- dispatch -----------------------------------------------------------------
 
 Tiling choose_tiling(int B, int G, int D) {
+  (void)D;
   const int M = B * G;
-  const int nt_max = (D >= 256) ? 3 : 6;
   const int tiles = (M + 15) / 16;
   Tiling t;
-  t.row_groups = (tiles + nt_max - 1) / nt_max;
-  int nt = (tiles + t.row_groups - 1) / t.row_groups;
-  if (nt == 5) nt = 6;
-  t.nt = nt;
+  t.row_groups = (tiles + 5) / 6;
+  const int per = (tiles + t.row_groups - 1) / t.row_groups;
+  t.nt = (per + 1) & ~1;  // even: the score waves take half the rows each
   return t;
 }
 
 bool partial_supported(int D, int kv_dtype, int nt) {
   if (kv_dtype != kQ8 && kv_dtype != kF16) return false;
   if (D != 64 && D != 128 && D != 256) return false;
-  if (D == 256) return nt >= 1 && nt <= 3;
-  return nt == 1 || nt == 2 || nt == 3 || nt == 4 || nt == 6;
+  return nt == 2 || nt == 4 || nt == 6;
 }
 
 template <int D, int KVT, int NT>
@@ -826,14 +869,10 @@ static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
 template <int D, int KVT>
 static hipError_t launch_nt(const PartialParams& p, int nt, hipStream_t stream) {
   switch (nt) {
-    case 1: return launch_t<D, KVT, 1>(p, stream);
     case 2: return launch_t<D, KVT, 2>(p, stream);
-    case 3: return launch_t<D, KVT, 3>(p, stream);
+    case 4: return launch_t<D, KVT, 4>(p, stream);
+    case 6: return launch_t<D, KVT, 6>(p, stream);
     default: break;
-  }
-  if constexpr (D <= 128) {
-    if (nt == 4) return launch_t<D, KVT, 4>(p, stream);
-    if (nt == 6) return launch_t<D, KVT, 6>(p, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -288,3 +288,15 @@ def test_bad_metadata_sets_flags_and_nans():
     got, lse, flags, _ = run_gpu(bad, 1, "f16", plan_splits=1, max_ctx=int(w.ctx_lens[0]))
     assert flags & va.VA_FLAG_BAD_CTX
     assert np.all(np.isnan(got))
+
+
+@pytest.mark.parametrize("ctx,S_", [(1024, 16), (1024, 32), (2048, 16), (1032, 13), (600, 3)])
+def test_short_splits(ctx, S_):
+    """Splits of one to three 64-key tiles, so the whole pipeline runs in its
+    prologue and drain (the first tile's pages are read right after issue)."""
+    say(f"[case] short splits ctx={ctx} S={S_}")
+    w = S.make_workload(f"short_{ctx}", ctx_lens=[ctx], B=16, H=24, KVH=4, D=256, q_dtype="bf16",
+                        kv_dtype="q8_0", seed=41, permute=True, spare_pages=5, poison=True)
+    ref, _ = oracle.attention(w)
+    got = run_gpu(w, S_, "f32")[0]
+    check_parity(got, ref, "f32", f"ctx={ctx} S={S_}")

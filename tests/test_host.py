@@ -58,11 +58,13 @@ def plan_status(problem, splits=0, cus=256):
 def test_headline_plan_and_workspace(lib):
     p = va.verify_attn_plan_for_cus(qwen(), 0, 256)
     info = p.info()
-    assert info.row_groups == 2 and info.rows_per_group == 48
-    assert info.num_splits == 32 and info.max_splits == 32
-    assert info.pages_per_split == 64
+    # one workgroup per (split, KV head) covers all 96 rows of the GQA group,
+    # so 64 splits x 4 KV heads fill the 256 CUs once
+    assert info.row_groups == 1 and info.rows_per_group == 96
+    assert info.num_splits == 64 and info.max_splits == 64
+    assert info.pages_per_split == 32
     nrows = 1 * 16 * 24
-    assert info.workspace_bytes == 256 + 32 * nrows * (256 + 2) * 4
+    assert info.workspace_bytes == 256 + 64 * nrows * (256 + 2) * 4
     assert p.workspace_bytes == info.workspace_bytes
 
 
@@ -84,9 +86,10 @@ def test_explicit_splits_and_direct(lib):
     assert p1.info().workspace_bytes == 256  # direct path needs only the flag header
 
 
-@pytest.mark.parametrize("B,G,D,nt,rg", [(16, 6, 256, 3, 2), (10, 6, 256, 2, 2), (32, 6, 256, 3, 4),
-                                         (4, 6, 256, 2, 1), (16, 6, 128, 6, 1), (4, 2, 64, 1, 1),
-                                         (64, 6, 256, 3, 8), (1, 1, 64, 1, 1)])
+@pytest.mark.parametrize("B,G,D,nt,rg", [(16, 6, 256, 6, 1), (10, 6, 256, 4, 1), (32, 6, 256, 6, 2),
+                                         (4, 6, 256, 2, 1), (16, 6, 128, 6, 1), (4, 2, 64, 2, 1),
+                                         (64, 6, 256, 6, 4), (1, 1, 64, 2, 1), (7, 6, 256, 4, 1),
+                                         (20, 6, 256, 4, 2), (33, 6, 128, 6, 3)])
 def test_row_tiling(lib, B, G, D, nt, rg):
     prob = qwen(rows_per_seq=B, num_q_heads=4 * G, head_dim=D)
     info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
