@@ -9,8 +9,11 @@ already resident in HBM.  Eight distinct KV pools (8 x 71 MB, well beyond the
 
 Prints one JSON line.  value = KV bytes of the valid tokens / time per call
 (GB/s); roofline = the partial kernel's algorithmic KV bytes / its average
-duration (HIP events on the launch stream) against the 8 TB/s HBM peak;
-cpu_baseline = the fp64 oracle timed on the host cores for one full call.
+duration (HIP events around back-to-back launches on the launch stream)
+against the 8 TB/s HBM peak, with the HBM traffic per launch measured by
+rocprofv3 counters (null once the kernel source differs from the profiled
+one) and the MFMA rate; cpu_baseline = the fp64 oracle timed on the host
+cores over a few full calls.
 """
 
 from __future__ import annotations
@@ -27,7 +30,28 @@ if ROOT not in sys.path:
 
 METRIC = "verify-attn µs/call + achieved HBM GB/s, B=16 H24/KV4/D256 Q8 KV ctx 32K"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 on MI355X
 NPOOLS = 8
+
+
+def traffic_from_profile(root):
+    """HBM bytes per partial launch from the committed counter summary, or None
+    when the partial kernel's source changed after the counters were taken."""
+    import hashlib
+    import re
+
+    prof = os.path.join(root, "profiles", "verify_partial_q8_b16_h24_kv4_d256_ctx32768_counters.md")
+    src = os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc", "verify_partial.hip")
+    try:
+        text = open(prof).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not m_sha or not m_val or m_sha.group(1) != digest:
+        return None
+    return int(m_val.group(1))
 
 
 def parse():
@@ -107,25 +131,27 @@ def main():
     ms_per_step = ms_total / args.steps
     gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # ---- per-kernel durations on the launch stream (same steps, events between launches) ----
+    # ---- per-kernel durations on the launch stream: each kernel timed over
+    # `steps` back-to-back launches between two events (the partial kernel
+    # still rotates the cold KV pools; the merge re-reads the last partials) ----
     S_used = info.num_splits
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        a, b, c = evs[i]
+
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record(stream)
-        step(i, "partial")
+        for i in range(args.steps):
+            fn(i)
         b.record(stream)
-        if S_used > 1:
-            va.verify_attn_run_merge(plan, 0, out, lse, ws, stream=stream)
-        c.record(stream)
-    torch.cuda.synchronize()
-    partial_ms = [a.elapsed_time(b) for a, b, _ in evs]
-    merge_ms = [b.elapsed_time(c) for _, b, c in evs]
-    partial_avg_us = 1e3 * sum(partial_ms) / len(partial_ms)
-    merge_avg_us = 1e3 * sum(merge_ms) / len(merge_ms)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / args.steps
+
+    partial_avg_us = timed(lambda i: step(i, "partial"))
+    merge_avg_us = timed(lambda i: va.verify_attn_run_merge(plan, 0, out, lse, ws, stream=stream)) if S_used > 1 else 0.0
     achieved = kv_bytes / (partial_avg_us * 1e-6) / 1e9
+    flops = 4.0 * w.D * w.H * sum(int(c) - w.B + (i + 1) for c in w.ctx_lens for i in range(w.B))
+    mfma_tflops = flops / (partial_avg_us * 1e-6) / 1e12
     flags = va.verify_attn_read_flags(plan, ws, stream)
 
     # ---- CPU baseline: the fp64 oracle on the host cores, one full call ----
@@ -134,12 +160,15 @@ def main():
         import oracle
 
         nthreads = oracle.default_threads()
+        calls = 0
         t0 = time.perf_counter()
-        oracle.attention(w, nthreads=nthreads)
-        dt = time.perf_counter() - t0
+        while calls < 5 and (calls == 0 or time.perf_counter() - t0 < 1.5):
+            oracle.attention(w, nthreads=nthreads)
+            calls += 1
+        dt = (time.perf_counter() - t0) / calls
         cpu = {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-               "sample": f"one full call of the same workload (all {w.num_seqs * w.B * w.H} row-heads, "
-                         f"ctx {args.ctx}), {dt:.2f} s wall on {nthreads} threads",
+               "sample": f"{calls} full calls of the same workload (all {w.num_seqs * w.B * w.H} row-heads, "
+                         f"ctx {args.ctx}), {dt:.2f} s wall each on {nthreads} threads",
                "seconds_per_call": dt}
 
     rec = {
@@ -160,9 +189,11 @@ def main():
                    "kv": "q8_0", "q": "bf16", "out": "f16", "splits": S_used, "row_groups": info.row_groups,
                    "kv_pools_rotated": args.pools, "kv_bytes_per_call": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "verify_partial_kernel<256,Q8,3>", "kernel_avg_us": round(partial_avg_us, 3),
-                     "merge_avg_us": round(merge_avg_us, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(ROOT),
+                     "kernel": "verify_partial_kernel<256,Q8,6>", "kernel_avg_us": round(partial_avg_us, 3),
+                     "merge_avg_us": round(merge_avg_us, 3),
+                     "mfma": {"tflops": round(mfma_tflops, 1), "peak_tflops": MFMA_PEAK_TFLOPS,
+                              "util": round(mfma_tflops / MFMA_PEAK_TFLOPS, 4)}},
         "cpu_baseline": cpu,
         "flags": flags,
     }

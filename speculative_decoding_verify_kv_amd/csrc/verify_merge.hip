@@ -10,10 +10,12 @@
 // 0 and their O is never used; a NaN l (a split that saw bad metadata) makes
 // the row NaN.
 //
-// One wave per (row, head).  Lane k first loads (m_k, l_k) of split k, so all
-// split headers arrive in one round trip; the weights are reduced across the
-// wave and kept in LDS.  Then each lane owns D/64 consecutive outputs and
-// streams the S partial rows in batches of 8 independent loads.
+// One workgroup of 4 waves per (row, head).  Wave w owns splits w, w + 4,
+// ...; it issues the loads of up to 16 of its split rows at once (16 bytes
+// per lane each at D = 256) before it reads the split headers, so the
+// partial rows are in flight while the weights are formed.  Every lane loads
+// the headers of splits lane, lane + 64, ... and the weight of split k is
+// taken from its owner lane with a shuffle.  The 4 waves' sums meet in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -45,53 +47,72 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int E> struct VecT { typedef float type __attribute__((ext_vector_type(E))); };
 template <> struct VecT<1> { typedef float type; };
 
-template <int D>
-__global__ __launch_bounds__(64) void verify_merge_kernel(const MergeParams p) {
-  constexpr int E = D / 64;  // outputs per lane
-  constexpr int BATCH = 8;
-  __shared__ float wts[kMaxSplits];
-  const int64_t R = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int S = p.S;
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 16;  // split rows in flight per wave
 
-  // split headers: lane k holds split k, k + 64, ...
+template <int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const MergeParams p) {
+  constexpr int E = D / 64;  // outputs per lane
+  constexpr int HJ = kMaxSplits / 64;
+  typedef typename VecT<E>::type vec;
+  __shared__ float red[kMergeWaves][D];
+  const int64_t R = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = p.S;
+  const float* base = p.part_o + R * D + E * lane;
+  const int64_t kstride = p.nrows * D;
+
+  auto load = [&](int k) __attribute__((always_inline)) -> vec {
+    return *reinterpret_cast<const vec*>(base + (int64_t)min(k, S - 1) * kstride);  // clamped: weight 0 below
+  };
+  vec v[kMergeBatch];
+#pragma unroll
+  for (int b = 0; b < kMergeBatch; ++b) v[b] = load(wave + kMergeWaves * b);
+
+  // split headers: lane holds splits lane + 64 j
+  float mh[HJ], lh[HJ];
   float M = -INFINITY;
   bool nan_row = false;
-  for (int k = lane; k < S; k += 64) {
-    const float l = p.part_l[(int64_t)k * p.nrows + R];
-    const float m = p.part_m[(int64_t)k * p.nrows + R];
-    nan_row |= (l != l);
-    if (l > 0.f) M = fmaxf(M, m);
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int k = lane + 64 * j;
+    mh[j] = -INFINITY;
+    lh[j] = 0.f;
+    if (k < S) {
+      mh[j] = p.part_m[(int64_t)k * p.nrows + R];
+      lh[j] = p.part_l[(int64_t)k * p.nrows + R];
+    }
+    nan_row |= (lh[j] != lh[j]);
+    if (lh[j] > 0.f) M = fmaxf(M, mh[j]);
   }
   M = wave_max(M);
   nan_row = __builtin_amdgcn_ballot_w64(nan_row) != 0;
+  float wh[HJ];
   float Lpart = 0.f;
-  for (int k = lane; k < S; k += 64) {
-    const float l = p.part_l[(int64_t)k * p.nrows + R];
-    const float w = (l > 0.f) ? __builtin_amdgcn_exp2f(p.part_m[(int64_t)k * p.nrows + R] - M) : 0.f;
-    wts[k] = w;
-    Lpart += w * l;
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    wh[j] = (lh[j] > 0.f) ? __builtin_amdgcn_exp2f(mh[j] - M) : 0.f;
+    Lpart += wh[j] * lh[j];
   }
   const float L = wave_sum(Lpart);
-  __syncthreads();
 
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  const float* base = p.part_o + R * D + E * lane;
-  const int64_t kstride = p.nrows * D;
-  typedef typename VecT<E>::type vec;
-  for (int k0 = 0; k0 < S; k0 += BATCH) {
-    vec v[BATCH];
+  for (int k0 = wave; k0 < S; k0 += kMergeWaves * kMergeBatch) {
+    if (k0 != wave) {
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int k = k0 + b < S ? k0 + b : S - 1;  // clamped: in bounds, weight 0 below
-      v[b] = *reinterpret_cast<const vec*>(base + (int64_t)k * kstride);
+      for (int b = 0; b < kMergeBatch; ++b) v[b] = load(k0 + kMergeWaves * b);
     }
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int k = k0 + b;
-      const float w = (k < S) ? wts[k] : 0.f;
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int k = k0 + kMergeWaves * b;  // wave-uniform
+      float w = 0.f;
+#pragma unroll
+      for (int j = 0; j < HJ; ++j)
+        if ((k >> 6) == j) w = __shfl(wh[j], k & 63);
+      if (k >= S) w = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float x;
@@ -101,12 +122,19 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(const MergeParams p) {
       }
     }
   }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[wave][E * lane + e] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;
 
   const float inv = nan_row ? __builtin_nanf("") : 1.0f / L;
   const int64_t o = R * D + E * lane;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float x = acc[e] * inv;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeWaves; ++w) sum += red[w][E * lane + e];
+    const float x = sum * inv;
     if (p.out_dtype == kF32) reinterpret_cast<float*>(p.out)[o + e] = x;
     else if (p.out_dtype == kF16) reinterpret_cast<h16*>(p.out)[o + e] = (h16)x;
     else reinterpret_cast<uint16_t*>(p.out)[o + e] = (uint16_t)f32_to_bf16_bits(x);
@@ -120,9 +148,9 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(const MergeParams p) {
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.nrows);
   switch (p.D) {
-    case 256: hipLaunchKernelGGL(verify_merge_kernel<256>, grid, dim3(64), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(verify_merge_kernel<128>, grid, dim3(64), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(verify_merge_kernel<64>, grid, dim3(64), 0, stream, p); break;
+    case 256: hipLaunchKernelGGL(verify_merge_kernel<256>, grid, dim3(64 * kMergeWaves), 0, stream, p); break;
+    case 128: hipLaunchKernelGGL(verify_merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, stream, p); break;
+    case 64: hipLaunchKernelGGL(verify_merge_kernel<64>, grid, dim3(64 * kMergeWaves), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
