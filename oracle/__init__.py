@@ -57,7 +57,11 @@ def _load():
         lib.orc_split_partials.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ctypes.c_int32, ip, dp, dp, dp,
                                            ctypes.c_int]
         lib.orc_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, dp, dp, dp, dp, dp]
-        for f in (lib.orc_attention, lib.orc_attention_items, lib.orc_split_partials, lib.orc_merge):
+        lib.orc_f32_to_f16.argtypes = [ctypes.c_int64, vp, vp]
+        lib.orc_quantize_blocks.argtypes = [ctypes.c_int64, vp, vp, vp]
+        lib.orc_append_kv.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ip, ip]
+        for f in (lib.orc_attention, lib.orc_attention_items, lib.orc_split_partials, lib.orc_merge,
+                  lib.orc_f32_to_f16, lib.orc_quantize_blocks, lib.orc_append_kv):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -155,3 +159,45 @@ def merge(m: np.ndarray, l: np.ndarray, o: np.ndarray):
     if rc != 0:
         raise OracleError("merge rejected the inputs (rc=%d)" % rc)
     return out, lse
+
+
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    """fp32 values -> IEEE binary16 bit patterns (uint16), round to nearest even."""
+    lib = _load()
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.zeros(x.shape, np.uint16)
+    lib.orc_f32_to_f16(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def quantize_blocks(x: np.ndarray):
+    """x [..., 32k] fp32 -> (q int8 same shape, d fp16 bits [..., k]) per 32-entry block."""
+    lib = _load()
+    x = np.ascontiguousarray(x, np.float32)
+    assert x.shape[-1] % 32 == 0
+    q = np.zeros(x.shape, np.int8)
+    d = np.zeros(x.shape[:-1] + (x.shape[-1] // 32,), np.uint16)
+    lib.orc_quantize_blocks(x.size // 32, _ptr(x), _ptr(q), _ptr(d))
+    return q, d
+
+
+def append_kv(w, k_new: np.ndarray, v_new: np.ndarray, new_dtype: str):
+    """Write the drafted rows' K/V (k_new, v_new [nseq*B, KVH, D]; new_dtype
+    "f32" | "f16" | "bf16", 16-bit inputs as raw bits) into copies of w's pools.
+    Returns (k_pool, v_pool, k_scale, v_scale) with scales as fp16 arrays (or None)."""
+    lib = _load()
+    shape, a = _prep(w)
+    k = a["k"].copy()
+    v = a["v"].copy()
+    ks = None if a["ks"] is None else a["ks"].copy()
+    vs = None if a["vs"] is None else a["vs"].copy()
+    kn = np.ascontiguousarray(k_new)
+    vn = np.ascontiguousarray(v_new)
+    if new_dtype in ("f16", "bf16"):
+        kn, vn = kn.view(np.uint16), vn.view(np.uint16)
+    rc = lib.orc_append_kv(ctypes.byref(shape), _DT[new_dtype], _ptr(kn), _ptr(vn), _ptr(k), _ptr(v), _ptr(ks),
+                           _ptr(vs), _ptr(a["bt"]), _ptr(a["ctx"]))
+    if rc != 0:
+        raise OracleError("oracle rejected the append (rc=%d)" % rc)
+    return (k.view(w.k_pool.dtype), v.view(w.v_pool.dtype), None if ks is None else ks.view(np.float16),
+            None if vs is None else vs.view(np.float16))

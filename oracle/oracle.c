@@ -406,3 +406,142 @@ int orc_merge(int32_t nsplit, int64_t nrows, int32_t D, const double* m, const d
   }
   return ORC_OK;
 }
+
+/* ---- KV append with 8-bit block quantisation (the step before verify) ----
+ *
+ * The B drafted rows' K and V vectors are written into their slots
+ * ctx_s - B + i of the paged pools (same layouts as above), before the verify
+ * attention reads them (page "perf(qwen35): retain speculation during paged
+ * prefill", State and commit invariants: the drafted rows' KV writes are shared
+ * by all row kinds).  8-bit pools store one fp16 scale per 32 consecutive
+ * head_dim entries with scale = max|x| / 127 of the block, computed in fp32
+ * and stored as fp16 round-to-nearest-even; codes
+ * q = clamp(round-half-away(x / d), -127, 127) with d the stored fp16 value,
+ * in fp32; an all-zero block stores d = 0 and q = 0; a NaN input stores code
+ * 0.  These decisions produce integers, so they are made in fp32, the
+ * precision the device kernel uses, not in fp64.  fp16 pools store the input
+ * rounded to nearest even.
+ */
+
+/* fp32 -> IEEE binary16 bits, round to nearest, ties to even. */
+static uint16_t f32_to_f16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);  /* NaN */
+  if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u); /* >= 65520: rounds to inf */
+  if (a >= 0x38800000u) {                                   /* |f| >= 2^-14: normal half */
+    const uint32_t mant = a & 0x7fffffu;
+    const uint32_t e = (a >> 23) - 127 + 15;
+    uint32_t h = (e << 10) | (mant >> 13);
+    const uint32_t rem = mant & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h++; /* a carry moves to the exponent */
+    return (uint16_t)(sign | h);
+  }
+  /* subnormal half: count units of 2^-24 */
+  const uint32_t E = a >> 23;
+  if (E == 0) return (uint16_t)sign; /* fp32 subnormal: far below 2^-25 */
+  const uint32_t m = (a & 0x7fffffu) | 0x800000u; /* value = m * 2^(E - 150) */
+  const uint32_t shift = 126 - E;                  /* value / 2^-24 = m >> shift */
+  if (shift >= 32) return (uint16_t)sign;
+  uint32_t q = m >> shift;
+  const uint32_t rem = m & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) q++;
+  return (uint16_t)(sign | q);
+}
+
+static float f16_to_f32(uint16_t h) { return (float)f16_to_double(h); }
+
+static float new_to_f32(int dtype, const void* x, int64_t idx) {
+  switch (dtype) {
+    case ORC_F32: return ((const float*)x)[idx];
+    case ORC_F16: return f16_to_f32(((const uint16_t*)x)[idx]);
+    default: return (float)bf16_to_double(((const uint16_t*)x)[idx]);
+  }
+}
+
+static void quantize_block(const float* x, int8_t* q, uint16_t* dbits) {
+  float amax = 0.0f;
+  for (int e = 0; e < 32; ++e) {
+    const float a = fabsf(x[e]);
+    if (a > amax) amax = a;
+  }
+  const float d = amax / 127.0f;
+  const uint16_t h = f32_to_f16_rne(d);
+  const float d16 = f16_to_f32(h);
+  for (int e = 0; e < 32; ++e) {
+    float r = 0.0f;
+    if (d16 != 0.0f) r = x[e] / d16;
+    if (r != r) r = 0.0f;
+    r = roundf(r);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    q[e] = (int8_t)r;
+  }
+  *dbits = h;
+}
+
+int orc_f32_to_f16(int64_t n, const float* x, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16_rne(x[i]);
+  return ORC_OK;
+}
+
+int orc_quantize_blocks(int64_t nblocks, const float* x, int8_t* q, uint16_t* d) {
+  for (int64_t b = 0; b < nblocks; ++b) quantize_block(x + 32 * b, q + 32 * b, d + b);
+  return ORC_OK;
+}
+
+int orc_append_kv(const orc_shape* p, int32_t new_dtype, const void* k_new, const void* v_new,
+                  void* k_pool, void* v_pool, uint16_t* k_scale, uint16_t* v_scale,
+                  const int32_t* block_table, const int32_t* ctx_lens) {
+  if (check_shape(p) != ORC_OK) return ORC_EINVAL;
+  if (p->kv_dtype != ORC_Q8 && p->kv_dtype != ORC_F16) return ORC_EINVAL;
+  if (new_dtype != ORC_F32 && new_dtype != ORC_F16 && new_dtype != ORC_BF16) return ORC_EINVAL;
+  for (int s = 0; s < p->num_seqs; ++s)
+    if (check_seq(p, block_table, ctx_lens, NULL, s) != ORC_OK) return ORC_EINVAL;
+  const int D = p->D, KVH = p->KVH, nb = D / 32;
+  float x[32];
+  int8_t q[32];
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int base = ctx_lens[s] - p->B;
+    for (int i = 0; i < p->B; ++i) {
+      const int t = base + i;
+      const int64_t page = block_table[(int64_t)s * p->max_pages + t / ORC_PAGE];
+      const int slot = t % ORC_PAGE;
+      for (int g = 0; g < KVH; ++g) {
+        const int64_t src = ((int64_t)(s * p->B + i) * KVH + g) * D;
+        const int64_t pk = (page * KVH + g) * ORC_PAGE * D; /* element offset of this page / head */
+        for (int which = 0; which < 2; ++which) {
+          const void* xin = which ? v_new : k_new;
+          if (p->kv_dtype == ORC_F16) {
+            uint16_t* pool = (uint16_t*)(which ? v_pool : k_pool);
+            for (int d = 0; d < D; ++d) {
+              const uint16_t h = f32_to_f16_rne(new_to_f32(new_dtype, xin, src + d));
+              if (which) pool[pk + (int64_t)d * ORC_PAGE + slot] = h;
+              else pool[pk + (int64_t)slot * D + d] = h;
+            }
+            continue;
+          }
+          int8_t* pool = (int8_t*)(which ? v_pool : k_pool);
+          uint16_t* sc = which ? v_scale : k_scale;
+          const int64_t ps = (page * KVH + g) * ORC_PAGE * nb; /* scale offset of this page / head */
+          for (int b = 0; b < nb; ++b) {
+            uint16_t dbits;
+            for (int e = 0; e < 32; ++e) x[e] = new_to_f32(new_dtype, xin, src + 32 * b + e);
+            quantize_block(x, q, &dbits);
+            for (int e = 0; e < 32; ++e) {
+              const int d = 32 * b + e;
+              if (which) pool[pk + (int64_t)d * ORC_PAGE + slot] = q[e];
+              else pool[pk + (int64_t)slot * D + d] = q[e];
+            }
+            if (which) sc[ps + (int64_t)b * ORC_PAGE + slot] = dbits;
+            else sc[ps + (int64_t)slot * nb + b] = dbits;
+          }
+        }
+      }
+    }
+  }
+  return ORC_OK;
+}

@@ -101,6 +101,24 @@ int orc_split_partials(const orc_shape* p, const void* q, const void* k_pool,
 int orc_merge(int32_t nsplit, int64_t nrows, int32_t D, const double* m, const double* l,
               const double* o, double* out, double* lse);
 
+/* fp32 -> IEEE binary16 bits, round to nearest even (n values). */
+int orc_f32_to_f16(int64_t n, const float* x, uint16_t* out);
+
+/* 8-bit block quantisation of nblocks blocks of 32 fp32 values:
+ * d = fp16(max|x| / 127) (fp32 arithmetic, fp16 RNE), q = clamp(round half
+ * away from zero (x / d), -127, 127) in fp32; all-zero block -> d = 0, q = 0;
+ * NaN -> code 0.  q [nblocks*32] int8, d [nblocks] fp16 bits. */
+int orc_quantize_blocks(int64_t nblocks, const float* x, int8_t* q, uint16_t* d);
+
+/* KV append: write the B drafted rows' K and V (k_new, v_new
+ * [num_seqs*B, KVH, D] in new_dtype: ORC_F32 | ORC_F16 | ORC_BF16) into slots
+ * ctx_s - B + i of the pools (kv_dtype ORC_Q8: int8 codes + fp16 scales as
+ * above; ORC_F16: fp16 RNE).  Returns ORC_EINVAL (nothing written) on bad
+ * metadata. */
+int orc_append_kv(const orc_shape* p, int32_t new_dtype, const void* k_new, const void* v_new,
+                  void* k_pool, void* v_pool, uint16_t* k_scale, uint16_t* v_scale,
+                  const int32_t* block_table, const int32_t* ctx_lens);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,4 +19,5 @@ from .workloads import (  # noqa: F401
     paged_ragged,
     tree_mixed,
     chain,
+    new_kv_rows,
 )

@@ -278,3 +278,20 @@ def chain(B: int, ctx: int = 20676, seed: int = 4, **kw) -> Workload:
     kw.setdefault("poison", True)
     return make_workload(f"chain_b{B}_h24_kv4_d256_q8_ctx{ctx}", ctx_lens=[ctx], B=B, H=24, KVH=4, D=256,
                          q_dtype="bf16", kv_dtype="q8_0", seed=seed, permute=True, **kw)
+
+
+def new_kv_rows(w: Workload, dtype: str = "f32", seed: int = 0):
+    """K and V vectors for the B drafted rows of every sequence, as a KV append
+    receives them: two arrays [num_seqs*B, KVH, D] of N(0,1) values in `dtype`
+    ("f32" float32, "f16" float16, "bf16" raw bfloat16 bits as uint16)."""
+    rng = np.random.default_rng(seed)
+    shape = (w.num_seqs * w.B, w.KVH, w.D)
+    out = []
+    for _ in range(2):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if dtype == "f16":
+            x = x.astype(np.float16)
+        elif dtype == "bf16":
+            x = bf16_bits_from_f32(x)
+        out.append(np.ascontiguousarray(x))
+    return out[0], out[1]
