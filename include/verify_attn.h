@@ -183,6 +183,32 @@ va_status verify_attn_run_partial(const va_plan* plan, const void* q, const void
 va_status verify_attn_run_merge(const va_plan* plan, int32_t num_splits, void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KV append: the step before verify_attn_run.  Writes the B drafted rows' K
+ * and V vectors of every sequence into their token slots ctx_lens[s] - B + i
+ * of the pools, converting them to the pool format (the drafted rows' KV
+ * writes precede the verify read: page "perf(qwen35): retain speculation
+ * during paged prefill", State and commit invariants).
+ *   k_new, v_new  [num_seqs*B, KVH, D] in new_dtype (VA_F32 | VA_F16 | VA_BF16),
+ *                 16-byte aligned, device memory, read only
+ *   k_pool ... v_scale, block_table, ctx_lens   as for verify_attn_run; the
+ *                 pools (and scales) are written at the drafted slots only
+ *   workspace     device buffer of at least 256 bytes (its flag word is used)
+ * VA_F16 pools receive the values rounded to nearest even.  VA_Q8_0 pools
+ * receive, per (token, KV head) and 32 consecutive head_dim entries, the fp16
+ * scale d = max|x| / 127 (fp32 arithmetic, rounded to nearest even) and the
+ * codes clamp(round half away from zero (x / d), -127, 127) computed in fp32
+ * with the stored d; an all-zero block stores d = 0 and zero codes, a NaN
+ * entry stores code 0.  A bad ctx_lens[s] or page id sets VA_FLAG_BAD_CTX /
+ * VA_FLAG_BAD_PAGE and that sequence's (or row's) writes are skipped; nothing
+ * outside the drafted slots is written.  Sequences must not share the pages
+ * that hold their drafted slots.
+ */
+va_status verify_attn_append_kv(const va_plan* plan, const void* k_new, const void* v_new, va_dtype new_dtype,
+                                void* k_pool, void* v_pool, void* k_scale, void* v_scale,
+                                const int32_t* block_table, const int32_t* ctx_lens, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Copy the workspace flag word to *flags (host) after synchronising `stream`,
  * then clear it on the device.  For tests and debugging; it blocks. */
 va_status verify_attn_read_flags(const va_plan* plan, void* workspace, void* stream, uint32_t* flags);

@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     verify_attn_plan,
     verify_attn_plan_for_cus,
     verify_attn_plan_get_info,
+    verify_attn_append_kv,
     verify_attn_read_flags,
     verify_attn_run,
     verify_attn_run_merge,

@@ -62,8 +62,8 @@ class VerifyAttnError(RuntimeError):
 _lib = None
 EXPORTED = (
     "verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_plan_destroy",
-    "verify_attn_run", "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_read_flags",
-    "verify_attn_status_string",
+    "verify_attn_run", "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv",
+    "verify_attn_read_flags", "verify_attn_status_string",
 )
 
 
@@ -89,11 +89,12 @@ def load(path: Optional[str] = None):
     lib.verify_attn_run.argtypes = run_args
     lib.verify_attn_run_partial.argtypes = run_args
     lib.verify_attn_run_merge.argtypes = [vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_append_kv.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_read_flags.argtypes = [vp, vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.verify_attn_status_string.argtypes = [i32]
     lib.verify_attn_status_string.restype = ctypes.c_char_p
     for n in ("verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_run",
-              "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_read_flags"):
+              "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv", "verify_attn_read_flags"):
         getattr(lib, n).restype = i32
     if path is None:
         _lib = lib
@@ -207,6 +208,17 @@ def verify_attn_run_merge(plan: Plan, num_splits, out, lse, workspace, workspace
                                       _stream(stream))
     if raise_on_error:
         _check(st, "verify_attn_run_merge")
+    return st
+
+
+def verify_attn_append_kv(plan: Plan, k_new, v_new, new_dtype: str, k_pool, v_pool, k_scale, v_scale, block_table,
+                          ctx_lens, workspace, workspace_bytes=None, stream=None, *, raise_on_error=True) -> int:
+    wsb = plan.workspace_bytes if workspace_bytes is None else int(workspace_bytes)
+    st = load().verify_attn_append_kv(plan.handle, _ptr(k_new), _ptr(v_new), DTYPE_CODES[new_dtype], _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table), _ptr(ctx_lens),
+                                      _ptr(workspace), wsb, _stream(stream))
+    if raise_on_error:
+        _check(st, "verify_attn_append_kv")
     return st
 
 

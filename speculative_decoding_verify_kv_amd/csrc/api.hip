@@ -272,6 +272,47 @@ va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool
   return VA_OK;
 }
 
+va_status verify_attn_append_kv(const va_plan* plan, const void* k_new, const void* v_new, va_dtype new_dtype,
+                                void* k_pool, void* v_pool, void* k_scale, void* v_scale,
+                                const int32_t* block_table, const int32_t* ctx_lens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!plan) return VA_EINVAL;
+  const va_problem& p = plan->prob;
+  if (new_dtype != VA_F32 && new_dtype != VA_F16 && new_dtype != VA_BF16) return VA_EINVAL;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !ctx_lens || !workspace) return VA_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(workspace, 256) || !aligned(block_table, 4) || !aligned(ctx_lens, 4))
+    return VA_EINVAL;
+  if (p.kv_dtype == VA_Q8_0) {
+    if (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16)) return VA_EINVAL;
+  } else if (k_scale || v_scale) {
+    return VA_EINVAL;
+  }
+  if (workspace_bytes < va::kHeaderBytes) return VA_EWORKSPACE;
+  va::AppendParams ap;
+  memset(&ap, 0, sizeof ap);
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.k_pool = k_pool;
+  ap.v_pool = v_pool;
+  ap.k_scale = k_scale;
+  ap.v_scale = v_scale;
+  ap.block_table = block_table;
+  ap.ctx_lens = ctx_lens;
+  ap.flags = static_cast<uint32_t*>(workspace);
+  ap.num_seqs = p.num_seqs;
+  ap.B = p.rows_per_seq;
+  ap.KVH = p.num_kv_heads;
+  ap.D = p.head_dim;
+  ap.num_pages = p.num_pages;
+  ap.max_pages = p.max_pages_per_seq;
+  ap.max_ctx = p.max_ctx;
+  ap.new_dtype = new_dtype;
+  ap.kv_dtype = p.kv_dtype;
+  if (va::launch_append(ap, static_cast<hipStream_t>(stream)) != hipSuccess) return VA_EHIP;
+  return VA_OK;
+}
+
 va_status verify_attn_read_flags(const va_plan* plan, void* workspace, void* stream, uint32_t* flags) {
   if (!plan || !workspace || !flags) return VA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -55,6 +55,21 @@ struct MergeParams {
   int64_t nrows;
 };
 
+struct AppendParams {
+  const void* k_new;      // [num_seqs*B, KVH, D] new_dtype
+  const void* v_new;
+  void* k_pool;
+  void* v_pool;
+  void* k_scale;          // 8-bit pools only
+  void* v_scale;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  uint32_t* flags;
+  int32_t num_seqs, B, KVH, D;
+  int32_t num_pages, max_pages, max_ctx;
+  int32_t new_dtype, kv_dtype;
+};
+
 // Tiling the plan picks for the partial kernel.
 struct Tiling {
   int nt;          // 16-row MFMA tiles per workgroup (2, 4 or 6)
@@ -66,6 +81,7 @@ bool partial_supported(int D, int kv_dtype, int nt);
 
 hipError_t launch_partial(const PartialParams& p, int kv_dtype, int nt, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 
 }  // namespace va
 

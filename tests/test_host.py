@@ -181,6 +181,31 @@ def test_merge_entry_checks(lib):
     assert f(plan, 8, FAKE, None, FAKE, 100, None, raise_on_error=False) == va.VA_EWORKSPACE
 
 
+def append_status(plan, **over):
+    a = dict(k_new=FAKE, v_new=FAKE, new_dtype="f32", k_pool=FAKE, v_pool=FAKE, k_scale=FAKE, v_scale=FAKE,
+             block_table=FAKE, ctx_lens=FAKE, workspace=FAKE, workspace_bytes=256)
+    a.update(over)
+    return va.verify_attn_append_kv(plan, a["k_new"], a["v_new"], a["new_dtype"], a["k_pool"], a["v_pool"],
+                                    a["k_scale"], a["v_scale"], a["block_table"], a["ctx_lens"], a["workspace"],
+                                    a["workspace_bytes"], None, raise_on_error=False)
+
+
+def test_append_rejects_bad_arguments(lib):
+    plan = va.verify_attn_plan_for_cus(qwen(), 8, 256)
+    assert append_status(plan, new_dtype="q8_0") == va.VA_EINVAL    # inputs are f32 / f16 / bf16
+    assert append_status(plan, k_new=None) == va.VA_EINVAL
+    assert append_status(plan, v_pool=None) == va.VA_EINVAL
+    assert append_status(plan, k_scale=None) == va.VA_EINVAL        # 8-bit pools need their scales
+    assert append_status(plan, k_new=FAKE + 4) == va.VA_EINVAL      # misaligned
+    assert append_status(plan, ctx_lens=FAKE + 2) == va.VA_EINVAL
+    assert append_status(plan, workspace=FAKE + 64) == va.VA_EINVAL
+    assert append_status(plan, workspace_bytes=255) == va.VA_EWORKSPACE
+    plan_f16 = va.verify_attn_plan_for_cus(qwen(kv_dtype="f16"), 8, 256)
+    assert append_status(plan_f16) == va.VA_EINVAL                  # fp16 pools take no scales
+    assert va.load().verify_attn_append_kv(None, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           256, None) == va.VA_EINVAL
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4):
         assert va.verify_attn_status_string(st)
