@@ -27,6 +27,8 @@ def to_device(w, device="cuda") -> Dict[str, object]:
         if a is None:
             return None
         a = np.ascontiguousarray(a)
+        if not a.flags.writeable:
+            a = a.copy()
         if a.dtype == np.uint16:  # bf16 bits
             return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
         return torch.from_numpy(a).to(device)
