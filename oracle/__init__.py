@@ -60,8 +60,9 @@ def _load():
         lib.orc_f32_to_f16.argtypes = [ctypes.c_int64, vp, vp]
         lib.orc_quantize_blocks.argtypes = [ctypes.c_int64, vp, vp, vp]
         lib.orc_append_kv.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ip, ip]
+        lib.orc_promote_kv.argtypes = [sp, ip, ip, ip, vp, vp, vp, vp, ip, ip, ip]
         for f in (lib.orc_attention, lib.orc_attention_items, lib.orc_split_partials, lib.orc_merge,
-                  lib.orc_f32_to_f16, lib.orc_quantize_blocks, lib.orc_append_kv):
+                  lib.orc_f32_to_f16, lib.orc_quantize_blocks, lib.orc_append_kv, lib.orc_promote_kv):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -201,3 +202,24 @@ def append_kv(w, k_new: np.ndarray, v_new: np.ndarray, new_dtype: str):
         raise OracleError("oracle rejected the append (rc=%d)" % rc)
     return (k.view(w.k_pool.dtype), v.view(w.v_pool.dtype), None if ks is None else ks.view(np.float16),
             None if vs is None else vs.view(np.float16))
+
+
+def promote_kv(w, accepted: np.ndarray, n_accepted: np.ndarray):
+    """Accepted-path promotion on copies of w's pools.  accepted [nseq, B]
+    (root-first drafted-row indices, entries past n_accepted ignored),
+    n_accepted [nseq].  Returns (k_pool, v_pool, k_scale, v_scale, new_ctx)."""
+    lib = _load()
+    shape, a = _prep(w)
+    k = a["k"].copy()
+    v = a["v"].copy()
+    ks = None if a["ks"] is None else a["ks"].copy()
+    vs = None if a["vs"] is None else a["vs"].copy()
+    acc = np.ascontiguousarray(accepted, np.int32).reshape(w.num_seqs, w.B)
+    n = np.ascontiguousarray(n_accepted, np.int32).reshape(w.num_seqs)
+    new_ctx = np.zeros(w.num_seqs, np.int32)
+    rc = lib.orc_promote_kv(ctypes.byref(shape), _ptr(acc), _ptr(n), _ptr(a["par"]), _ptr(k), _ptr(v), _ptr(ks),
+                            _ptr(vs), _ptr(a["bt"]), _ptr(a["ctx"]), _ptr(new_ctx))
+    if rc != 0:
+        raise OracleError("oracle rejected the promotion (rc=%d)" % rc)
+    return (k.view(w.k_pool.dtype), v.view(w.v_pool.dtype), None if ks is None else ks.view(np.float16),
+            None if vs is None else vs.view(np.float16), new_ctx)

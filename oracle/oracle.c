@@ -545,3 +545,102 @@ int orc_append_kv(const orc_shape* p, int32_t new_dtype, const void* k_new, cons
   }
   return ORC_OK;
 }
+
+/* ---- accepted-path KV promotion (the step after verify, tree mode) ----
+ *
+ * After the tree rows are verified, the caller picks for each sequence an
+ * accepted path r_0, ..., r_{n-1} of drafted rows (root first, each node the
+ * child of the previous one: parent[r_k] == r_{k-1}).  Promotion copies their
+ * K / V vectors (and 8-bit scales) to the consecutive slots that directly
+ * follow the first node's parent, dst = base + parent[r_0] + 1 (base when the
+ * parent is -1), so the durable prefix then reads as the accepted tokens in
+ * order; new_ctx = dst + n.  Every sequence is checked before any pool byte
+ * changes, and on any failure nothing is written (the page "perf(qwen35):
+ * retain speculation during paged prefill", State and commit invariants:
+ * promotion moves only the accepted prefix and preflights before mutating).
+ * Sources and destinations may overlap; the copy goes through a buffer.
+ */
+static int64_t slot_elem(int kv_dtype_is_v, int64_t page, int KVH, int g, int D, int slot, int d) {
+  const int64_t head = (page * KVH + g) * ORC_PAGE * D;
+  return kv_dtype_is_v ? head + (int64_t)d * ORC_PAGE + slot : head + (int64_t)slot * D + d;
+}
+
+int orc_promote_kv(const orc_shape* p, const int32_t* accepted, const int32_t* n_accepted,
+                   const int32_t* parent, void* k_pool, void* v_pool, uint16_t* k_scale,
+                   uint16_t* v_scale, const int32_t* block_table, const int32_t* ctx_lens,
+                   int32_t* new_ctx) {
+  if (check_shape(p) != ORC_OK) return ORC_EINVAL;
+  if (p->kv_dtype != ORC_Q8 && p->kv_dtype != ORC_F16) return ORC_EINVAL;
+  const int B = p->B, D = p->D, KVH = p->KVH, nb = D / 32;
+  /* preflight: every sequence, before any write */
+  for (int s = 0; s < p->num_seqs; ++s) {
+    if (check_seq(p, block_table, ctx_lens, parent, s) != ORC_OK) return ORC_EINVAL;
+    const int n = n_accepted[s];
+    if (n < 0 || n > B) return ORC_EINVAL;
+    for (int k = 0; k < n; ++k) {
+      const int r = accepted[(int64_t)s * B + k];
+      if (r < 0 || r >= B) return ORC_EINVAL;
+      const int par = parent ? parent[(int64_t)s * B + r] : r - 1;
+      if (k > 0 && par != accepted[(int64_t)s * B + k - 1]) return ORC_EINVAL;
+    }
+  }
+  const int esz = p->kv_dtype == ORC_Q8 ? 1 : 2;
+  unsigned char* kbuf = (unsigned char*)malloc((size_t)B * KVH * D * esz);
+  unsigned char* vbuf = (unsigned char*)malloc((size_t)B * KVH * D * esz);
+  uint16_t* ksbuf = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * KVH * nb + 2);
+  uint16_t* vsbuf = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * KVH * nb + 2);
+  if (!kbuf || !vbuf || !ksbuf || !vsbuf) {
+    free(kbuf); free(vbuf); free(ksbuf); free(vsbuf);
+    return ORC_EINVAL;
+  }
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int n = n_accepted[s];
+    const int base = ctx_lens[s] - B;
+    const int32_t* bt = block_table + (int64_t)s * p->max_pages;
+    int dst = base;
+    if (n > 0) {
+      const int r0 = accepted[(int64_t)s * B];
+      const int par0 = parent ? parent[(int64_t)s * B + r0] : r0 - 1;
+      dst = base + par0 + 1;
+    }
+    /* gather the accepted rows */
+    for (int k = 0; k < n; ++k) {
+      const int t = base + accepted[(int64_t)s * B + k];
+      const int64_t page = bt[t / ORC_PAGE];
+      const int slot = t % ORC_PAGE;
+      for (int g = 0; g < KVH; ++g) {
+        for (int d = 0; d < D; ++d) {
+          const int64_t kb = ((int64_t)(k * KVH + g) * D + d) * esz;
+          memcpy(kbuf + kb, (unsigned char*)k_pool + slot_elem(0, page, KVH, g, D, slot, d) * esz, esz);
+          memcpy(vbuf + kb, (unsigned char*)v_pool + slot_elem(1, page, KVH, g, D, slot, d) * esz, esz);
+        }
+        if (p->kv_dtype == ORC_Q8)
+          for (int b = 0; b < nb; ++b) {
+            ksbuf[(k * KVH + g) * nb + b] = k_scale[((page * KVH + g) * ORC_PAGE + slot) * nb + b];
+            vsbuf[(k * KVH + g) * nb + b] = v_scale[((page * KVH + g) * nb + b) * ORC_PAGE + slot];
+          }
+      }
+    }
+    /* write them to the consecutive slots after the anchor */
+    for (int k = 0; k < n; ++k) {
+      const int t = dst + k;
+      const int64_t page = bt[t / ORC_PAGE];
+      const int slot = t % ORC_PAGE;
+      for (int g = 0; g < KVH; ++g) {
+        for (int d = 0; d < D; ++d) {
+          const int64_t kb = ((int64_t)(k * KVH + g) * D + d) * esz;
+          memcpy((unsigned char*)k_pool + slot_elem(0, page, KVH, g, D, slot, d) * esz, kbuf + kb, esz);
+          memcpy((unsigned char*)v_pool + slot_elem(1, page, KVH, g, D, slot, d) * esz, vbuf + kb, esz);
+        }
+        if (p->kv_dtype == ORC_Q8)
+          for (int b = 0; b < nb; ++b) {
+            k_scale[((page * KVH + g) * ORC_PAGE + slot) * nb + b] = ksbuf[(k * KVH + g) * nb + b];
+            v_scale[((page * KVH + g) * nb + b) * ORC_PAGE + slot] = vsbuf[(k * KVH + g) * nb + b];
+          }
+      }
+    }
+    if (new_ctx) new_ctx[s] = dst + n;
+  }
+  free(kbuf); free(vbuf); free(ksbuf); free(vsbuf);
+  return ORC_OK;
+}

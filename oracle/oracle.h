@@ -119,6 +119,18 @@ int orc_append_kv(const orc_shape* p, int32_t new_dtype, const void* k_new, cons
                   void* k_pool, void* v_pool, uint16_t* k_scale, uint16_t* v_scale,
                   const int32_t* block_table, const int32_t* ctx_lens);
 
+/* Accepted-path KV promotion: for each sequence copy the K / V (and scales)
+ * of drafted rows accepted[s][0..n_accepted[s]) -- a root-first path,
+ * parent[r_k] == r_{k-1} -- to the consecutive slots starting right after the
+ * first node's parent slot (dst = ctx - B + parent[r_0] + 1); new_ctx[s] =
+ * dst + n (optional).  All sequences are validated before any write;
+ * ORC_EINVAL and nothing written on failure.  accepted [num_seqs, B],
+ * n_accepted [num_seqs], parent [num_seqs, B] or NULL (chain). */
+int orc_promote_kv(const orc_shape* p, const int32_t* accepted, const int32_t* n_accepted,
+                   const int32_t* parent, void* k_pool, void* v_pool, uint16_t* k_scale,
+                   uint16_t* v_scale, const int32_t* block_table, const int32_t* ctx_lens,
+                   int32_t* new_ctx);
+
 #ifdef __cplusplus
 }
 #endif
