@@ -98,6 +98,7 @@ typedef enum { VA_F32 = 0, VA_F16 = 1, VA_BF16 = 2, VA_Q8_0 = 3 } va_dtype;
 #define VA_FLAG_BAD_CTX 0x1u    /* ctx_lens[s] < B, > max_ctx, or beyond the block table */
 #define VA_FLAG_BAD_PAGE 0x2u   /* block_table entry outside [0, num_pages) */
 #define VA_FLAG_BAD_PARENT 0x4u /* parent[s][i] outside [-1, i) */
+#define VA_FLAG_BAD_PATH 0x8u   /* promotion: accepted rows not a root-first parent chain, or n outside [0, B] */
 
 typedef struct {
   int32_t num_seqs;          /* >= 1 */
@@ -208,6 +209,40 @@ va_status verify_attn_append_kv(const va_plan* plan, const void* k_new, const vo
                                 void* k_pool, void* v_pool, void* k_scale, void* v_scale,
                                 const int32_t* block_table, const int32_t* ctx_lens, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Accepted-path KV promotion: the step after verification in tree mode.  For
+ * each sequence s the caller names the accepted path
+ *   accepted[s][0 .. n_accepted[s])   drafted-row indices, root first, each
+ *                                     the child of the previous one
+ *                                     (parent[s][r_k] == r_{k-1})
+ * The K / V vectors (and 8-bit scales) of those rows move, in path order, to
+ * the consecutive slots right after the first row's parent:
+ *   dst = ctx_lens[s] - B + parent[s][r_0] + 1   (ctx_lens[s] - B when -1)
+ * and new_ctx[s] = dst + n_accepted[s], the length of the durable prefix now
+ * holding the accepted tokens (n_accepted[s] == 0 gives ctx_lens[s] - B).
+ * Only the accepted rows move (page "perf(qwen35): retain speculation during
+ * paged prefill", State and commit invariants: promotion moves the accepted
+ * prefix and preflights all state before mutating).  Every sequence is
+ * checked on the device before any pool byte changes: a bad path, ctx, parent
+ * or page id sets VA_FLAG_BAD_PATH / _CTX / _PARENT / _PAGE, nothing is
+ * written to any pool, and new_ctx[s] = ctx_lens[s] for every s.
+ *   accepted, n_accepted     [num_seqs, B] / [num_seqs] int32, device
+ *   parent                   [num_seqs, B] or NULL (chain), device
+ *   new_ctx                  [num_seqs] int32 output, device, optional (NULL)
+ *   workspace                device, 256-byte aligned, at least
+ *                            verify_attn_promote_workspace_bytes(plan) bytes:
+ *                            flag word at byte 0, this call's check word at
+ *                            byte 4, staging of the accepted rows after 256
+ * Sources and destinations may overlap (the rows are staged first).
+ */
+va_status verify_attn_promote_kv(const va_plan* plan, const int32_t* accepted, const int32_t* n_accepted,
+                                 const int32_t* parent, void* k_pool, void* v_pool, void* k_scale, void* v_scale,
+                                 const int32_t* block_table, const int32_t* ctx_lens, int32_t* new_ctx,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes verify_attn_promote_kv needs for this plan (0 if plan is NULL). */
+size_t verify_attn_promote_workspace_bytes(const va_plan* plan);
 
 /* Copy the workspace flag word to *flags (host) after synchronising `stream`,
  * then clear it on the device.  For tests and debugging; it blocks. */

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     VA_FLAG_BAD_CTX,
     VA_FLAG_BAD_PAGE,
     VA_FLAG_BAD_PARENT,
+    VA_FLAG_BAD_PATH,
     VA_OK,
     Plan,
     VaPlanInfo,
@@ -28,6 +29,8 @@ from ._binding import (  # noqa: F401
     verify_attn_plan_for_cus,
     verify_attn_plan_get_info,
     verify_attn_append_kv,
+    verify_attn_promote_kv,
+    verify_attn_promote_workspace_bytes,
     verify_attn_read_flags,
     verify_attn_run,
     verify_attn_run_merge,

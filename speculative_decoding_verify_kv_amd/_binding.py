@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libverify_attn.so")
 
 VA_OK, VA_EINVAL, VA_EUNSUPPORTED, VA_EWORKSPACE, VA_EHIP = 0, -1, -2, -3, -4
 VA_F32, VA_F16, VA_BF16, VA_Q8_0 = 0, 1, 2, 3
-VA_FLAG_BAD_CTX, VA_FLAG_BAD_PAGE, VA_FLAG_BAD_PARENT = 0x1, 0x2, 0x4
+VA_FLAG_BAD_CTX, VA_FLAG_BAD_PAGE, VA_FLAG_BAD_PARENT, VA_FLAG_BAD_PATH = 0x1, 0x2, 0x4, 0x8
 
 DTYPE_CODES = {"f32": VA_F32, "f16": VA_F16, "bf16": VA_BF16, "q8_0": VA_Q8_0}
 
@@ -63,7 +63,8 @@ _lib = None
 EXPORTED = (
     "verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_plan_destroy",
     "verify_attn_run", "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv",
-    "verify_attn_read_flags", "verify_attn_status_string",
+    "verify_attn_promote_kv", "verify_attn_promote_workspace_bytes", "verify_attn_read_flags",
+    "verify_attn_status_string",
 )
 
 
@@ -90,11 +91,15 @@ def load(path: Optional[str] = None):
     lib.verify_attn_run_partial.argtypes = run_args
     lib.verify_attn_run_merge.argtypes = [vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_append_kv.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_promote_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_promote_workspace_bytes.argtypes = [vp]
+    lib.verify_attn_promote_workspace_bytes.restype = ctypes.c_size_t
     lib.verify_attn_read_flags.argtypes = [vp, vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     lib.verify_attn_status_string.argtypes = [i32]
     lib.verify_attn_status_string.restype = ctypes.c_char_p
     for n in ("verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_run",
-              "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv", "verify_attn_read_flags"):
+              "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv", "verify_attn_promote_kv",
+              "verify_attn_read_flags"):
         getattr(lib, n).restype = i32
     if path is None:
         _lib = lib
@@ -219,6 +224,22 @@ def verify_attn_append_kv(plan: Plan, k_new, v_new, new_dtype: str, k_pool, v_po
                                       _ptr(workspace), wsb, _stream(stream))
     if raise_on_error:
         _check(st, "verify_attn_append_kv")
+    return st
+
+
+def verify_attn_promote_workspace_bytes(plan: Plan) -> int:
+    return int(load().verify_attn_promote_workspace_bytes(plan.handle))
+
+
+def verify_attn_promote_kv(plan: Plan, accepted, n_accepted, parent, k_pool, v_pool, k_scale, v_scale, block_table,
+                           ctx_lens, new_ctx, workspace, workspace_bytes=None, stream=None, *,
+                           raise_on_error=True) -> int:
+    wsb = verify_attn_promote_workspace_bytes(plan) if workspace_bytes is None else int(workspace_bytes)
+    st = load().verify_attn_promote_kv(plan.handle, _ptr(accepted), _ptr(n_accepted), _ptr(parent), _ptr(k_pool),
+                                       _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_table),
+                                       _ptr(ctx_lens), _ptr(new_ctx), _ptr(workspace), wsb, _stream(stream))
+    if raise_on_error:
+        _check(st, "verify_attn_promote_kv")
     return st
 
 

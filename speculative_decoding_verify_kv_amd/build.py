@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverify_attn.so")
-SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip", "append_kv.hip"]
+SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip", "append_kv.hip", "promote_kv.hip"]
 # The partial kernel keeps its O accumulators in VGPRs and lets the Q operand
 # fragments sit in AGPRs (MFMA reads A/B from AGPRs); the default heuristic
 # instead shuttles the accumulators through AGPR spill slots every iteration.

@@ -313,6 +313,61 @@ va_status verify_attn_append_kv(const va_plan* plan, const void* k_new, const vo
   return VA_OK;
 }
 
+size_t verify_attn_promote_workspace_bytes(const va_plan* plan) {
+  if (!plan) return 0;
+  const va_problem& p = plan->prob;
+  return va::kHeaderBytes + (size_t)p.num_seqs * p.rows_per_seq * p.num_kv_heads * 2 *
+                                va::promote_row_bytes(p.head_dim, p.kv_dtype);
+}
+
+va_status verify_attn_promote_kv(const va_plan* plan, const int32_t* accepted, const int32_t* n_accepted,
+                                 const int32_t* parent, void* k_pool, void* v_pool, void* k_scale, void* v_scale,
+                                 const int32_t* block_table, const int32_t* ctx_lens, int32_t* new_ctx,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return VA_EINVAL;
+  const va_problem& p = plan->prob;
+  if (!accepted || !n_accepted || !k_pool || !v_pool || !block_table || !ctx_lens || !workspace) return VA_EINVAL;
+  if (!aligned(accepted, 4) || !aligned(n_accepted, 4) || (parent && !aligned(parent, 4)) ||
+      (new_ctx && !aligned(new_ctx, 4)) || !aligned(block_table, 4) || !aligned(ctx_lens, 4) ||
+      !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(workspace, 256))
+    return VA_EINVAL;
+  if (p.kv_dtype == VA_Q8_0) {
+    if (!k_scale || !v_scale || !aligned(k_scale, 16) || !aligned(v_scale, 16)) return VA_EINVAL;
+  } else if (k_scale || v_scale) {
+    return VA_EINVAL;
+  }
+  if ((p.has_parent != 0) != (parent != nullptr)) return VA_EINVAL;
+  if (workspace_bytes < verify_attn_promote_workspace_bytes(plan)) return VA_EWORKSPACE;
+  va::PromoteParams pp;
+  memset(&pp, 0, sizeof pp);
+  pp.accepted = accepted;
+  pp.n_accepted = n_accepted;
+  pp.parent = parent;
+  pp.k_pool = k_pool;
+  pp.v_pool = v_pool;
+  pp.k_scale = k_scale;
+  pp.v_scale = v_scale;
+  pp.block_table = block_table;
+  pp.ctx_lens = ctx_lens;
+  pp.new_ctx = new_ctx;
+  char* ws = static_cast<char*>(workspace);
+  pp.flags = reinterpret_cast<uint32_t*>(ws);
+  pp.status = reinterpret_cast<uint32_t*>(ws + 4);
+  pp.staging = ws + va::kHeaderBytes;
+  pp.row_bytes = (int64_t)va::promote_row_bytes(p.head_dim, p.kv_dtype);
+  pp.num_seqs = p.num_seqs;
+  pp.B = p.rows_per_seq;
+  pp.KVH = p.num_kv_heads;
+  pp.D = p.head_dim;
+  pp.num_pages = p.num_pages;
+  pp.max_pages = p.max_pages_per_seq;
+  pp.max_ctx = p.max_ctx;
+  pp.esz = p.kv_dtype == VA_Q8_0 ? 1 : 2;
+  pp.kv_is_q8 = p.kv_dtype == VA_Q8_0 ? 1 : 0;
+  if (va::launch_promote(pp, static_cast<hipStream_t>(stream)) != hipSuccess) return VA_EHIP;
+  return VA_OK;
+}
+
 va_status verify_attn_read_flags(const va_plan* plan, void* workspace, void* stream, uint32_t* flags) {
   if (!plan || !workspace || !flags) return VA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -70,6 +70,26 @@ struct AppendParams {
   int32_t new_dtype, kv_dtype;
 };
 
+struct PromoteParams {
+  const int32_t* accepted;   // [num_seqs, B] root-first path rows
+  const int32_t* n_accepted; // [num_seqs]
+  const int32_t* parent;     // [num_seqs, B] or NULL (chain)
+  void* k_pool;
+  void* v_pool;
+  void* k_scale;             // 8-bit pools only
+  void* v_scale;
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int32_t* new_ctx;          // [num_seqs] or NULL
+  uint32_t* flags;           // cumulative workspace flag word
+  uint32_t* status;          // this call's check word
+  char* staging;             // num_seqs * B * KVH * 2 rows of row_bytes
+  int64_t row_bytes;
+  int32_t num_seqs, B, KVH, D;
+  int32_t num_pages, max_pages, max_ctx;
+  int32_t esz, kv_is_q8;
+};
+
 // Tiling the plan picks for the partial kernel.
 struct Tiling {
   int nt;          // 16-row MFMA tiles per workgroup (2, 4 or 6)
@@ -82,6 +102,8 @@ bool partial_supported(int D, int kv_dtype, int nt);
 hipError_t launch_partial(const PartialParams& p, int kv_dtype, int nt, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+size_t promote_row_bytes(int D, int kv_dtype);
+hipError_t launch_promote(const PromoteParams& p, hipStream_t stream);
 
 }  // namespace va
 

@@ -206,6 +206,34 @@ def test_append_rejects_bad_arguments(lib):
                                            256, None) == va.VA_EINVAL
 
 
+def promote_status(plan, **over):
+    a = dict(accepted=FAKE, n_accepted=FAKE, parent=None, k_pool=FAKE, v_pool=FAKE, k_scale=FAKE, v_scale=FAKE,
+             block_table=FAKE, ctx_lens=FAKE, new_ctx=None, workspace=FAKE,
+             workspace_bytes=va.verify_attn_promote_workspace_bytes(plan))
+    a.update(over)
+    return va.verify_attn_promote_kv(plan, a["accepted"], a["n_accepted"], a["parent"], a["k_pool"], a["v_pool"],
+                                     a["k_scale"], a["v_scale"], a["block_table"], a["ctx_lens"], a["new_ctx"],
+                                     a["workspace"], a["workspace_bytes"], None, raise_on_error=False)
+
+
+def test_promote_workspace_and_rejections(lib):
+    plan = va.verify_attn_plan_for_cus(qwen(), 8, 256)
+    # 256-byte header + per (row, KV head, K or V) one staged row: D int8 + D/32 fp16 scales, 16-byte rounded
+    assert va.verify_attn_promote_workspace_bytes(plan) == 256 + 1 * 16 * 4 * 2 * 272
+    assert promote_status(plan, workspace_bytes=va.verify_attn_promote_workspace_bytes(plan) - 1) == va.VA_EWORKSPACE
+    assert promote_status(plan, accepted=None) == va.VA_EINVAL
+    assert promote_status(plan, parent=FAKE) == va.VA_EINVAL          # has_parent == 0
+    assert promote_status(plan, k_scale=None) == va.VA_EINVAL
+    assert promote_status(plan, new_ctx=FAKE + 2) == va.VA_EINVAL
+    assert promote_status(plan, workspace=FAKE + 128) == va.VA_EINVAL
+    plan_p = va.verify_attn_plan_for_cus(qwen(has_parent=True), 8, 256)
+    assert promote_status(plan_p) == va.VA_EINVAL                     # parent required
+    plan_f16 = va.verify_attn_plan_for_cus(qwen(kv_dtype="f16"), 8, 256)
+    assert va.verify_attn_promote_workspace_bytes(plan_f16) == 256 + 1 * 16 * 4 * 2 * 512
+    assert promote_status(plan_f16) == va.VA_EINVAL                   # fp16 pools take no scales
+    assert va.load().verify_attn_promote_workspace_bytes(None) == 0
+
+
 def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4):
         assert va.verify_attn_status_string(st)
