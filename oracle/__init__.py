@@ -51,11 +51,11 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, dp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
         sp = ctypes.POINTER(_Shape)
-        lib.orc_attention.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, dp, dp, ctypes.c_int]
-        lib.orc_attention_items.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ctypes.c_int32, ip, dp, dp,
+        lib.orc_attention.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ip, dp, dp, ctypes.c_int]
+        lib.orc_attention_items.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ctypes.c_int32, ip, dp, dp,
                                             ctypes.c_int]
-        lib.orc_split_partials.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ctypes.c_int32, ip, dp, dp, dp,
-                                           ctypes.c_int]
+        lib.orc_split_partials.argtypes = [sp, vp, vp, vp, vp, vp, ip, ip, ip, ip, ctypes.c_int32, ip, dp, dp,
+                                           dp, ctypes.c_int]
         lib.orc_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, dp, dp, dp, dp, dp]
         lib.orc_f32_to_f16.argtypes = [ctypes.c_int64, vp, vp]
         lib.orc_quantize_blocks.argtypes = [ctypes.c_int64, vp, vp, vp]
@@ -87,6 +87,7 @@ def _prep(w):
         bt=np.ascontiguousarray(w.block_table, dtype=np.int32),
         ctx=np.ascontiguousarray(w.ctx_lens, dtype=np.int32),
         par=None if w.parent is None else np.ascontiguousarray(w.parent, dtype=np.int32),
+        cu=None if getattr(w, "cu_rows", None) is None else np.ascontiguousarray(w.cu_rows, dtype=np.int32),
     )
     if w.q_dtype in ("f16", "bf16"):
         arrs["q"] = arrs["q"].view(np.uint16)
@@ -95,7 +96,13 @@ def _prep(w):
 
 def _common(a):
     return (_ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["ks"]), _ptr(a["vs"]), _ptr(a["bt"]),
-            _ptr(a["ctx"]), _ptr(a["par"]))
+            _ptr(a["ctx"]), _ptr(a["par"]), _ptr(a["cu"]))
+
+
+def total_rows(w) -> int:
+    """Packed query rows of a workload: num_seqs*B, or cu_rows[-1] when ragged."""
+    cu = getattr(w, "cu_rows", None)
+    return w.num_seqs * w.B if cu is None else int(cu[-1])
 
 
 def default_threads() -> int:
@@ -103,11 +110,11 @@ def default_threads() -> int:
 
 
 def attention(w, nthreads: Optional[int] = None):
-    """Definition evaluated in fp64 -> (out [nseq*B, H, D], lse [nseq*B, H])."""
+    """Definition evaluated in fp64 -> (out [rows, H, D], lse [rows, H])."""
     lib = _load()
     shape, a = _prep(w)
-    out = np.zeros((w.num_seqs * w.B, w.H, w.D), np.float64)
-    lse = np.zeros((w.num_seqs * w.B, w.H), np.float64)
+    out = np.zeros((total_rows(w), w.H, w.D), np.float64)
+    lse = np.zeros((total_rows(w), w.H), np.float64)
     rc = lib.orc_attention(ctypes.byref(shape), *_common(a), _ptr(out), _ptr(lse),
                            nthreads or default_threads())
     if rc != 0:
@@ -116,7 +123,7 @@ def attention(w, nthreads: Optional[int] = None):
 
 
 def attention_items(w, items: Sequence[Sequence[int]], nthreads: Optional[int] = None):
-    """Definition for chosen (seq, row, head) triples -> (out [n, D], lse [n])."""
+    """Definition for chosen (seq, sequence-local row, head) triples -> (out [n, D], lse [n])."""
     lib = _load()
     shape, a = _prep(w)
     it = np.ascontiguousarray(np.asarray(items, np.int32).reshape(-1, 3))
@@ -135,7 +142,7 @@ def split_partials(w, bounds: np.ndarray, nthreads: Optional[int] = None):
     shape, a = _prep(w)
     b = np.ascontiguousarray(bounds, np.int32)
     S = b.shape[1] - 1
-    nrows = w.num_seqs * w.B * w.H
+    nrows = total_rows(w) * w.H
     m = np.zeros((S, nrows), np.float64)
     l = np.zeros((S, nrows), np.float64)
     o = np.zeros((S, nrows, w.D), np.float64)
@@ -187,6 +194,8 @@ def append_kv(w, k_new: np.ndarray, v_new: np.ndarray, new_dtype: str):
     "f32" | "f16" | "bf16", 16-bit inputs as raw bits) into copies of w's pools.
     Returns (k_pool, v_pool, k_scale, v_scale) with scales as fp16 arrays (or None)."""
     lib = _load()
+    if getattr(w, "cu_rows", None) is not None:
+        raise OracleError("KV append / promotion take B rows per sequence, not ragged rows")
     shape, a = _prep(w)
     k = a["k"].copy()
     v = a["v"].copy()
@@ -209,6 +218,8 @@ def promote_kv(w, accepted: np.ndarray, n_accepted: np.ndarray):
     (root-first drafted-row indices, entries past n_accepted ignored),
     n_accepted [nseq].  Returns (k_pool, v_pool, k_scale, v_scale, new_ctx)."""
     lib = _load()
+    if getattr(w, "cu_rows", None) is not None:
+        raise OracleError("KV append / promotion take B rows per sequence, not ragged rows")
     shape, a = _prep(w)
     k = a["k"].copy()
     v = a["v"].copy()

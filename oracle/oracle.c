@@ -59,30 +59,43 @@ static int check_shape(const orc_shape* p) {
   return ORC_OK;
 }
 
+/* Sequence s has n query rows; par_s (NULL = chain) is its slice of parent. */
 static int check_seq(const orc_shape* p, const int32_t* bt, const int32_t* ctx_lens,
-                     const int32_t* parent, int s) {
+                     const int32_t* par_s, int n, int s) {
   int ctx = ctx_lens[s];
-  if (ctx < p->B || ctx > p->max_pages * ORC_PAGE) return ORC_EINVAL;
+  if (ctx < n || ctx > p->max_pages * ORC_PAGE) return ORC_EINVAL;
   for (int pg = 0; pg < (ctx + ORC_PAGE - 1) / ORC_PAGE; ++pg) {
     int id = bt[(int64_t)s * p->max_pages + pg];
     if (id < 0 || id >= p->num_pages) return ORC_EINVAL;
   }
-  if (parent) {
-    for (int i = 0; i < p->B; ++i) {
-      int par = parent[(int64_t)s * p->B + i];
+  if (par_s) {
+    for (int i = 0; i < n; ++i) {
+      int par = par_s[i];
       if (par < -1 || par >= i) return ORC_EINVAL;
     }
   }
   return ORC_OK;
 }
 
-/* anc[i*B + a] = 1 iff in-window row a is row i or one of its ancestors. */
-static void build_ancestry(const int32_t* par_s, int B, unsigned char* anc) {
-  memset(anc, 0, (size_t)B * B);
-  for (int i = 0; i < B; ++i) {
+/* Rows of sequence s: count n and first packed row row0.  Without cu_rows
+ * every sequence has B rows; with it, rows cu_rows[s] .. cu_rows[s+1]. */
+static void seq_rows(const orc_shape* p, const int32_t* cu_rows, int s, int* n, int64_t* row0) {
+  if (cu_rows) {
+    *row0 = cu_rows[s];
+    *n = cu_rows[s + 1] - cu_rows[s];
+  } else {
+    *row0 = (int64_t)s * p->B;
+    *n = p->B;
+  }
+}
+
+/* anc[i*n + a] = 1 iff in-window row a is row i or one of its ancestors. */
+static void build_ancestry(const int32_t* par_s, int n, unsigned char* anc) {
+  memset(anc, 0, (size_t)n * n);
+  for (int i = 0; i < n; ++i) {
     int a = i;
     while (a >= 0) {
-      anc[i * B + a] = 1;
+      anc[(int64_t)i * n + a] = 1;
       a = par_s ? par_s[a] : a - 1;
     }
   }
@@ -132,17 +145,19 @@ typedef struct {
   const double* V;
   const unsigned char* anc;
   int s, ctx;
+  int n;       /* query rows of this sequence; they sit at slots ctx - n + i */
+  int64_t row0; /* packed index of its row 0 in q / out */
 } seq_ctx;
 
 static int visible(const seq_ctx* c, int i, int j) {
-  int base = c->ctx - c->p->B;
+  int base = c->ctx - c->n;
   if (j < base) return 1;
-  return c->anc[i * c->p->B + (j - base)];
+  return c->anc[(int64_t)i * c->n + (j - base)];
 }
 
 static double score(const seq_ctx* c, int i, int h, int j) {
   const orc_shape* p = c->p;
-  int64_t qrow = ((int64_t)(c->s * p->B + i) * p->H + h) * p->D;
+  int64_t qrow = ((c->row0 + i) * p->H + h) * p->D;
   double acc = 0.0;
   for (int d = 0; d < p->D; ++d) acc += load_q(p, c->q, qrow + d) * c->K[(int64_t)j * p->D + d];
   return p->scale * acc;
@@ -221,7 +236,7 @@ static void* run_job(void* arg) {
   double* z = (double*)malloc(sizeof(double) * (size_t)(c->ctx > 0 ? c->ctx : 1));
   for (int w = jb->tid; w < jb->n_work; w += jb->nthreads) {
     int i = jb->work[2 * w], h = jb->work[2 * w + 1];
-    int64_t row = (int64_t)(c->s * p->B + i) * p->H + h; /* (seq*B + i, h) */
+    int64_t row = (c->row0 + i) * p->H + h; /* (packed row, head) */
     if (jb->mode == 0) {
       attend_direct(c, i, h, z, jb->out + row * p->D, jb->lse + row);
     } else if (jb->mode == 2) {
@@ -264,13 +279,26 @@ static void run_parallel(job* proto, int nthreads) {
  * requested (row, head) items. */
 static int drive(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
                  const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* bt,
-                 const int32_t* ctx_lens, const int32_t* parent, int mode, int32_t n_items,
-                 const int32_t* items, double* out, double* lse, int32_t nsplit,
+                 const int32_t* ctx_lens, const int32_t* parent, const int32_t* cu_rows, int mode,
+                 int32_t n_items, const int32_t* items, double* out, double* lse, int32_t nsplit,
                  const int32_t* bounds, double* m, double* l, double* o, int nthreads) {
   if (check_shape(p) != ORC_OK) return ORC_EINVAL;
   if (p->kv_dtype == ORC_Q8 && (!k_scale || !v_scale)) return ORC_EINVAL;
-  for (int s = 0; s < p->num_seqs; ++s)
-    if (check_seq(p, bt, ctx_lens, parent, s) != ORC_OK) return ORC_EINVAL;
+  if (cu_rows) {
+    if (cu_rows[0] != 0) return ORC_EINVAL;
+    for (int s = 0; s < p->num_seqs; ++s)
+      if (cu_rows[s + 1] < cu_rows[s]) return ORC_EINVAL;
+  }
+  int n_max = 0;
+  int64_t total_rows = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    int n;
+    int64_t row0;
+    seq_rows(p, cu_rows, s, &n, &row0);
+    if (check_seq(p, bt, ctx_lens, parent ? parent + row0 : NULL, n, s) != ORC_OK) return ORC_EINVAL;
+    if (n > n_max) n_max = n;
+    total_rows = row0 + n;
+  }
   if (mode == 1) {
     if (nsplit < 1) return ORC_EINVAL;
     for (int s = 0; s < p->num_seqs; ++s) {
@@ -283,14 +311,19 @@ static int drive(const orc_shape* p, const void* q, const void* k_pool, const vo
   if (mode == 2) {
     for (int t = 0; t < n_items; ++t) {
       int s = items[3 * t], i = items[3 * t + 1], h = items[3 * t + 2];
-      if (s < 0 || s >= p->num_seqs || i < 0 || i >= p->B || h < 0 || h >= p->H) return ORC_EINVAL;
+      if (s < 0 || s >= p->num_seqs || h < 0 || h >= p->H) return ORC_EINVAL;
+      int n;
+      int64_t row0;
+      seq_rows(p, cu_rows, s, &n, &row0);
+      if (i < 0 || i >= n) return ORC_EINVAL;
     }
   }
 
   const int G = p->H / p->KVH;
-  const int64_t nrows_total = (int64_t)p->num_seqs * p->B * p->H;
-  unsigned char* anc = (unsigned char*)malloc((size_t)p->B * p->B);
-  int32_t* work = (int32_t*)malloc(sizeof(int32_t) * 2 * (size_t)(p->B * G > n_items ? p->B * G : n_items + 1));
+  const int64_t nrows_total = total_rows * p->H;
+  const int64_t n_anc = n_max > 0 ? (int64_t)n_max * n_max : 1;
+  unsigned char* anc = (unsigned char*)malloc((size_t)n_anc);
+  int32_t* work = (int32_t*)malloc(sizeof(int32_t) * 2 * (size_t)(n_max * G > n_items ? n_max * G : n_items + 1));
   int32_t* widx = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_items + 1));
   if (!anc || !work || !widx) {
     free(anc); free(work); free(widx);
@@ -299,7 +332,10 @@ static int drive(const orc_shape* p, const void* q, const void* k_pool, const vo
   int rc = ORC_OK;
   for (int s = 0; s < p->num_seqs && rc == ORC_OK; ++s) {
     int ctx = ctx_lens[s];
-    build_ancestry(parent ? parent + (int64_t)s * p->B : NULL, p->B, anc);
+    int n;
+    int64_t row0;
+    seq_rows(p, cu_rows, s, &n, &row0);
+    build_ancestry(parent ? parent + row0 : NULL, n, anc);
     for (int g = 0; g < p->KVH; ++g) {
       int n_work = 0;
       if (mode == 2) {
@@ -312,7 +348,7 @@ static int drive(const orc_shape* p, const void* q, const void* k_pool, const vo
         }
       } else {
         for (int hh = 0; hh < G; ++hh)
-          for (int i = 0; i < p->B; ++i) {
+          for (int i = 0; i < n; ++i) {
             work[2 * n_work] = i;
             work[2 * n_work + 1] = g * G + hh;
             ++n_work;
@@ -327,7 +363,7 @@ static int drive(const orc_shape* p, const void* q, const void* k_pool, const vo
         break;
       }
       decode_seq_kv(p, k_pool, v_pool, k_scale, v_scale, bt, s, g, ctx, K, V);
-      seq_ctx c = {p, q, K, V, anc, s, ctx};
+      seq_ctx c = {p, q, K, V, anc, s, ctx, n, row0};
       job proto;
       memset(&proto, 0, sizeof proto);
       proto.c = &c;
@@ -358,29 +394,29 @@ static int drive(const orc_shape* p, const void* q, const void* k_pool, const vo
 
 int orc_attention(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
                   const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
-                  const int32_t* ctx_lens, const int32_t* parent, double* out, double* lse,
-                  int nthreads) {
-  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, 0, 0, NULL,
-               out, lse, 0, NULL, NULL, NULL, NULL, nthreads);
+                  const int32_t* ctx_lens, const int32_t* parent, const int32_t* cu_rows,
+                  double* out, double* lse, int nthreads) {
+  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, cu_rows, 0, 0,
+               NULL, out, lse, 0, NULL, NULL, NULL, NULL, nthreads);
 }
 
 int orc_attention_items(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
                         const uint16_t* k_scale, const uint16_t* v_scale,
                         const int32_t* block_table, const int32_t* ctx_lens,
-                        const int32_t* parent, int32_t n_items, const int32_t* items,
-                        double* out, double* lse, int nthreads) {
+                        const int32_t* parent, const int32_t* cu_rows, int32_t n_items,
+                        const int32_t* items, double* out, double* lse, int nthreads) {
   if (n_items < 0 || (n_items > 0 && !items)) return ORC_EINVAL;
-  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, 2, n_items,
-               items, out, lse, 0, NULL, NULL, NULL, NULL, nthreads);
+  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, cu_rows, 2,
+               n_items, items, out, lse, 0, NULL, NULL, NULL, NULL, nthreads);
 }
 
 int orc_split_partials(const orc_shape* p, const void* q, const void* k_pool,
                        const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
                        const int32_t* block_table, const int32_t* ctx_lens,
-                       const int32_t* parent, int32_t nsplit, const int32_t* bounds, double* m,
-                       double* l, double* o, int nthreads) {
-  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, 1, 0, NULL,
-               NULL, NULL, nsplit, bounds, m, l, o, nthreads);
+                       const int32_t* parent, const int32_t* cu_rows, int32_t nsplit,
+                       const int32_t* bounds, double* m, double* l, double* o, int nthreads) {
+  return drive(p, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, cu_rows, 1, 0,
+               NULL, NULL, NULL, nsplit, bounds, m, l, o, nthreads);
 }
 
 int orc_merge(int32_t nsplit, int64_t nrows, int32_t D, const double* m, const double* l,
@@ -500,7 +536,7 @@ int orc_append_kv(const orc_shape* p, int32_t new_dtype, const void* k_new, cons
   if (p->kv_dtype != ORC_Q8 && p->kv_dtype != ORC_F16) return ORC_EINVAL;
   if (new_dtype != ORC_F32 && new_dtype != ORC_F16 && new_dtype != ORC_BF16) return ORC_EINVAL;
   for (int s = 0; s < p->num_seqs; ++s)
-    if (check_seq(p, block_table, ctx_lens, NULL, s) != ORC_OK) return ORC_EINVAL;
+    if (check_seq(p, block_table, ctx_lens, NULL, p->B, s) != ORC_OK) return ORC_EINVAL;
   const int D = p->D, KVH = p->KVH, nb = D / 32;
   float x[32];
   int8_t q[32];
@@ -574,7 +610,8 @@ int orc_promote_kv(const orc_shape* p, const int32_t* accepted, const int32_t* n
   const int B = p->B, D = p->D, KVH = p->KVH, nb = D / 32;
   /* preflight: every sequence, before any write */
   for (int s = 0; s < p->num_seqs; ++s) {
-    if (check_seq(p, block_table, ctx_lens, parent, s) != ORC_OK) return ORC_EINVAL;
+    if (check_seq(p, block_table, ctx_lens, parent ? parent + (int64_t)s * B : NULL, B, s) != ORC_OK)
+      return ORC_EINVAL;
     const int n = n_accepted[s];
     if (n < 0 || n > B) return ORC_EINVAL;
     for (int k = 0; k < n; ++k) {

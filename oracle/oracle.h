@@ -26,6 +26,15 @@
  *     M = max z_j,  L = sum e^(z_j - M),  O = sum e^(z_j - M) V_j / L,
  *     lse = M + ln L                                           (natural log)
  *
+ *   Ragged rows (cu_rows != NULL; the page "perf(qwen35): retain speculation
+ *   during paged prefill", Mechanism: one step lowers paged ragged prefill
+ *   segments, ordinary direct rows and fixed-width tree rows together):
+ *   sequence s owns the packed rows cu_rows[s] .. cu_rows[s+1] - 1 of q / out,
+ *   n_s = cu_rows[s+1] - cu_rows[s] >= 0 of them, row i at slot ctx_s - n_s + i,
+ *   and B above reads n_s, s*B + i reads cu_rows[s] + i.  parent is then
+ *   packed the same way ([total_rows], sequence-local indices).  A prefill
+ *   segment or a direct row is a chain; a tree is a parent array.
+ *
  *   Split form (partials then log-sum-exp merge), any token partition
  *   0 = b_0 <= b_1 <= ... <= b_S = ctx_s:
  *     m_k = max z over Vis within [b_{k-1}, b_k)   (-inf if empty)
@@ -35,7 +44,9 @@
  *
  * Memory layouts (C-contiguous, the same documented contract the HIP library
  * accepts, re-implemented here from that description):
- *   q        [num_seqs*B, H, D]          f32 | f16 | bf16
+ *   q        [num_seqs*B, H, D]          f32 | f16 | bf16  ([total_rows, H, D] ragged)
+ *   parent   [num_seqs, B] int32 or NULL ([total_rows] ragged)
+ *   cu_rows  [num_seqs + 1] int32 or NULL (cu_rows[0] = 0, non-decreasing)
  *   k_pool   [num_pages, KVH, 16, D]     token-major        (f32 | f16 | int8)
  *   v_pool   [num_pages, KVH, D, 16]     dim-major          (f32 | f16 | int8)
  *   k_scale  [num_pages, KVH, 16, D/32]  f16 bits (8-bit pools only)
@@ -44,7 +55,7 @@
  *   block_table [num_seqs, max_pages] int32; token j of seq s lives in page
  *   block_table[s][j/16], slot j%16.
  *
- * Errors: every function returns ORC_OK or ORC_EINVAL (ctx_s < B or beyond
+ * Errors: every function returns ORC_OK or ORC_EINVAL (ctx_s < n_s or beyond
  * the block table, parent outside [-1, i), page id outside [0, num_pages),
  * D not a multiple of 32 for 8-bit pools, H not a multiple of KVH).
  */
@@ -73,28 +84,28 @@ typedef struct {
 } orc_shape;
 
 /* Direct (definition) evaluation for every (row, head).
- * out [num_seqs*B, H, D], lse [num_seqs*B, H]. */
+ * out [rows, H, D], lse [rows, H]; rows = num_seqs*B, or cu_rows[num_seqs]. */
 int orc_attention(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
                   const uint16_t* k_scale, const uint16_t* v_scale, const int32_t* block_table,
-                  const int32_t* ctx_lens, const int32_t* parent, double* out, double* lse,
-                  int nthreads);
+                  const int32_t* ctx_lens, const int32_t* parent, const int32_t* cu_rows,
+                  double* out, double* lse, int nthreads);
 
-/* Same definition for a chosen set of (seq, row, head) triples only.
- * items [n_items*3]; out [n_items, D]; lse [n_items]. */
+/* Same definition for a chosen set of (seq, row, head) triples only (row is
+ * sequence-local).  items [n_items*3]; out [n_items, D]; lse [n_items]. */
 int orc_attention_items(const orc_shape* p, const void* q, const void* k_pool, const void* v_pool,
                         const uint16_t* k_scale, const uint16_t* v_scale,
                         const int32_t* block_table, const int32_t* ctx_lens,
-                        const int32_t* parent, int32_t n_items, const int32_t* items,
-                        double* out, double* lse, int nthreads);
+                        const int32_t* parent, const int32_t* cu_rows, int32_t n_items,
+                        const int32_t* items, double* out, double* lse, int nthreads);
 
 /* Split partials over a caller-chosen token partition.
  * bounds [num_seqs, nsplit+1] (b_0 = 0, b_nsplit = ctx_s, non-decreasing).
- * m, l [nsplit, num_seqs*B, H]; o [nsplit, num_seqs*B, H, D]. */
+ * m, l [nsplit, rows, H]; o [nsplit, rows, H, D] (rows as for orc_attention). */
 int orc_split_partials(const orc_shape* p, const void* q, const void* k_pool,
                        const void* v_pool, const uint16_t* k_scale, const uint16_t* v_scale,
                        const int32_t* block_table, const int32_t* ctx_lens,
-                       const int32_t* parent, int32_t nsplit, const int32_t* bounds, double* m,
-                       double* l, double* o, int nthreads);
+                       const int32_t* parent, const int32_t* cu_rows, int32_t nsplit,
+                       const int32_t* bounds, double* m, double* l, double* o, int nthreads);
 
 /* Log-sum-exp merge of split partials (empty splits have l == 0 and are skipped).
  * m, l [nsplit, nrows]; o [nsplit, nrows, D]; out [nrows, D]; lse [nrows]. */

@@ -19,5 +19,7 @@ from .workloads import (  # noqa: F401
     paged_ragged,
     tree_mixed,
     chain,
+    chain_parent,
+    mixed_lowering,
     new_kv_rows,
 )

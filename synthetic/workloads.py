@@ -10,6 +10,7 @@ take only their shapes.
 Memory layouts produced (all C-contiguous):
 
   q         [num_seqs*B, H, D]            float32 | float16 | bf16 bits (uint16)
+                                          ([total_rows, H, D] with ragged rows)
   k_pool    [num_pages, KVH, 16, D]       token-major rows
   v_pool    [num_pages, KVH, D, 16]       dim-major (the 16 tokens of a page are
                                           contiguous for each dimension)
@@ -19,6 +20,11 @@ Memory layouts produced (all C-contiguous):
   ctx_lens  [num_seqs]                    int32, counts every valid token,
                                           including the B drafted rows
   parent    [num_seqs, B] int32 or None   -1 <= parent[i] < i
+                                          ([total_rows] with ragged rows)
+  cu_rows   [num_seqs + 1] int32 or None  ragged rows: sequence s owns packed
+                                          rows cu_rows[s] .. cu_rows[s+1] - 1,
+                                          the last tokens of its context; B is
+                                          then the largest per-sequence count
 
 An 8-bit pool stores x ~= d * q with one float16 scale d per 32 consecutive
 head_dim indices of one (token, KV head): d = max|x| / 127 (computed in
@@ -89,6 +95,17 @@ class Workload:
     ctx_lens: np.ndarray
     parent: Optional[np.ndarray]
     seed: int = 0
+    cu_rows: Optional[np.ndarray] = None
+
+    @property
+    def total_rows(self) -> int:
+        return self.num_seqs * self.B if self.cu_rows is None else int(self.cu_rows[-1])
+
+    def seq_rows(self, s: int):
+        """(first packed row, row count) of sequence s."""
+        if self.cu_rows is None:
+            return s * self.B, self.B
+        return int(self.cu_rows[s]), int(self.cu_rows[s + 1] - self.cu_rows[s])
 
     @property
     def max_ctx(self) -> int:
@@ -123,7 +140,7 @@ def make_workload(
     name: str,
     *,
     ctx_lens: Sequence[int],
-    B: int,
+    B: int = 0,
     H: int,
     KVH: int,
     D: int,
@@ -138,16 +155,32 @@ def make_workload(
     q_gain: float = 1.0,
     scale: Optional[float] = None,
     max_pages: Optional[int] = None,
+    rows: Optional[Sequence[int]] = None,
 ) -> Workload:
+    """rows: per-sequence query-row counts (ragged); then B is their maximum
+    and parent, when given, is packed per row."""
     rng = np.random.default_rng(seed)
     nseq = len(ctx_lens)
     ctx = np.asarray(ctx_lens, dtype=np.int32)
-    if np.any(ctx < B):
-        raise ValueError("every context must hold the B drafted rows")
+    cu_rows = None
+    if rows is not None:
+        n = np.asarray(rows, dtype=np.int32)
+        if n.shape != (nseq,) or np.any(n < 0):
+            raise ValueError("rows needs one non-negative count per sequence")
+        cu_rows = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        B = max(int(n.max()), 1)
+        need = n
+    else:
+        need = np.full(nseq, B)
+    if B < 1:
+        raise ValueError("B must be at least 1")
+    if np.any(ctx < need):
+        raise ValueError("every context must hold its query rows")
     if D % 32:
         raise ValueError("head_dim must be a multiple of 32")
+    total = nseq * B if cu_rows is None else int(cu_rows[-1])
 
-    qf = (rng.standard_normal((nseq * B, H, D), dtype=np.float32) * np.float32(q_gain)).astype(np.float32)
+    qf = (rng.standard_normal((total, H, D), dtype=np.float32) * np.float32(q_gain)).astype(np.float32)
     if q_dtype == "f32":
         q = qf
     elif q_dtype == "f16":
@@ -215,7 +248,10 @@ def make_workload(
             v_pool[pg[:, None], np.arange(KVH)[None, :], :, sl[:, None]] = vf.astype(npdt)
 
     if parent is not None:
-        parent = np.ascontiguousarray(np.broadcast_to(np.asarray(parent, np.int32), (nseq, B)))
+        if cu_rows is None:
+            parent = np.ascontiguousarray(np.broadcast_to(np.asarray(parent, np.int32), (nseq, B)))
+        else:
+            parent = np.ascontiguousarray(np.asarray(parent, np.int32).reshape(total))
     if scale is None:
         scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
     return Workload(
@@ -223,7 +259,7 @@ def make_workload(
         max_pages=max_pages, q_dtype=q_dtype, kv_dtype=kv_dtype, out_dtype=out_dtype,
         scale=float(np.float32(scale)), q=q, k_pool=k_pool, v_pool=v_pool,
         k_scale=k_scale, v_scale=v_scale, block_table=block_table, ctx_lens=ctx,
-        parent=parent, seed=seed,
+        parent=parent, seed=seed, cu_rows=cu_rows,
     )
 
 
@@ -278,6 +314,32 @@ def chain(B: int, ctx: int = 20676, seed: int = 4, **kw) -> Workload:
     kw.setdefault("poison", True)
     return make_workload(f"chain_b{B}_h24_kv4_d256_q8_ctx{ctx}", ctx_lens=[ctx], B=B, H=24, KVH=4, D=256,
                          q_dtype="bf16", kv_dtype="q8_0", seed=seed, permute=True, **kw)
+
+
+def chain_parent(n: int) -> np.ndarray:
+    """Parent array of n positioned causal rows (prefill segment or direct rows)."""
+    return np.arange(-1, n - 1, dtype=np.int32)
+
+
+def mixed_lowering(seed: int = 5, prefill=(100, 37), prefill_ctx=(1016, 1032),
+                   direct_ctx=(1024, 40000), tree_ctx: int = 20676, n_direct: int = 2, n_tree: int = 8,
+                   **kw) -> Workload:
+    """One call holding the three row kinds of a mixed step, in order:
+    paged ragged prefill segments (chains of `prefill` rows ending at their
+    contexts), established decoders with one direct row each, and one
+    sequence of n_direct direct rows plus a width-n_tree draft tree.  Contexts
+    straddle the 1,024-token (64-page) boundary.  24/4 heads, D=256, 8-bit
+    paged KV in one permuted, NaN-poisoned pool; parent packed per row."""
+    rng = np.random.default_rng(seed + 2000)
+    rows = list(prefill) + [1] * len(direct_ctx) + [n_direct + n_tree]
+    ctxs = list(prefill_ctx) + list(direct_ctx) + [tree_ctx]
+    par = [chain_parent(n) for n in rows[:-1]] + [tree_parent(n_direct, n_tree, rng)]
+    kw.setdefault("poison", True)
+    kw.setdefault("spare_pages", 11)
+    name = "mixed_prefill{}_direct{}_tree{}+{}_h24_kv4_d256_q8".format(
+        "-".join(map(str, prefill)), len(direct_ctx), n_direct, n_tree)
+    return make_workload(name, ctx_lens=ctxs, rows=rows, H=24, KVH=4, D=256, q_dtype="bf16",
+                         kv_dtype="q8_0", seed=seed, permute=True, parent=np.concatenate(par), **kw)
 
 
 def new_kv_rows(w: Workload, dtype: str = "f32", seed: int = 0):

@@ -52,33 +52,52 @@ def ancestor_sets(parent_row, B):
     return sets
 
 
+def rows_of(w, s: int):
+    """(first packed row, count) of sequence s, uniform or ragged."""
+    cu = getattr(w, "cu_rows", None)
+    if cu is None:
+        return s * w.B, w.B
+    return int(cu[s]), int(cu[s + 1]) - int(cu[s])
+
+
+def parent_slice(w, s: int):
+    if w.parent is None:
+        return None
+    r0, n = rows_of(w, s)
+    return w.parent[s] if getattr(w, "cu_rows", None) is None else w.parent[r0:r0 + n]
+
+
 def visibility(w, s: int) -> np.ndarray:
     ctx = int(w.ctx_lens[s])
-    base = ctx - w.B
-    anc = ancestor_sets(None if w.parent is None else w.parent[s], w.B)
-    vis = np.zeros((w.B, ctx), bool)
+    _, n = rows_of(w, s)
+    base = ctx - n
+    anc = ancestor_sets(parent_slice(w, s), n)
+    vis = np.zeros((n, ctx), bool)
     vis[:, :base] = True
-    for i in range(w.B):
+    for i in range(n):
         for a in anc[i]:
             vis[i, base + a] = True
     return vis
 
 
 def attention(w):
-    Q = decode_q(w).reshape(w.num_seqs, w.B, w.H, w.D)
+    Q = decode_q(w).reshape(-1, w.H, w.D)
     G = w.H // w.KVH
-    out = np.zeros((w.num_seqs, w.B, w.H, w.D))
-    lse = np.zeros((w.num_seqs, w.B, w.H))
+    out = np.zeros((Q.shape[0], w.H, w.D))
+    lse = np.zeros((Q.shape[0], w.H))
     for s in range(w.num_seqs):
+        r0, n = rows_of(w, s)
+        if n == 0:
+            continue
         K, V = gather_kv(w, s)
         vis = visibility(w, s)
         for h in range(w.H):
             g = h // G
-            z = w.scale * (Q[s, :, h, :] @ K[:, g, :].T)          # [B, ctx]
+            z = w.scale * (Q[r0:r0 + n, h, :] @ K[:, g, :].T)     # [n, ctx]
             z = np.where(vis, z, -np.inf)
             M = z.max(axis=1, keepdims=True)
             e = np.exp(z - M)
             L = e.sum(axis=1, keepdims=True)
-            out[s, :, h, :] = (e @ V[:, g, :]) / L
-            lse[s, :, h] = (M + np.log(L))[:, 0]
-    return out.reshape(w.num_seqs * w.B, w.H, w.D), lse.reshape(w.num_seqs * w.B, w.H)
+            out[r0:r0 + n, h, :] = (e @ V[:, g, :]) / L
+            lse[r0:r0 + n, h] = (M + np.log(L))[:, 0]
+    return out, lse
