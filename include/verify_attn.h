@@ -99,6 +99,7 @@ typedef enum { VA_F32 = 0, VA_F16 = 1, VA_BF16 = 2, VA_Q8_0 = 3 } va_dtype;
 #define VA_FLAG_BAD_PAGE 0x2u   /* block_table entry outside [0, num_pages) */
 #define VA_FLAG_BAD_PARENT 0x4u /* parent[s][i] outside [-1, i) */
 #define VA_FLAG_BAD_PATH 0x8u   /* promotion: accepted rows not a root-first parent chain, or n outside [0, B] */
+#define VA_FLAG_BAD_ROWS 0x10u  /* ragged: cu_rows not non-decreasing from >= 0, a count above rows_per_seq, or past max_total_rows */
 
 typedef struct {
   int32_t num_seqs;          /* >= 1 */
@@ -115,6 +116,10 @@ typedef struct {
   va_dtype out_dtype;        /* VA_F16 | VA_BF16 | VA_F32 */
   float scale;               /* softmax scale; 0 => 1/sqrt(D) in fp32 */
   int32_t has_parent;        /* 0: causal rows (parent must be NULL); 1: parent array required */
+  int32_t max_total_rows;    /* 0: B rows per sequence (verify_attn_run).  > 0: ragged rows
+                                (verify_attn_run_ragged): rows_per_seq is then the largest
+                                per-sequence count (1..4096) and this the packed row capacity,
+                                at most num_seqs * rows_per_seq */
 } va_problem;
 
 typedef struct va_plan va_plan; /* opaque, host-only, immutable */
@@ -160,13 +165,45 @@ void verify_attn_plan_destroy(va_plan* plan);
  *   num_splits  0 = the plan's choice; else 1..max_splits
  *   workspace   device buffer of at least the plan's workspace_bytes
  * Pointers as in MEMORY LAYOUTS; k_scale / v_scale must be NULL unless
- * kv_dtype is VA_Q8_0; parent must be NULL iff has_parent == 0.
+ * kv_dtype is VA_Q8_0; parent must be NULL iff has_parent == 0.  Plans with
+ * max_total_rows > 0 are refused (VA_EINVAL): they run through
+ * verify_attn_run_ragged.  So are they by the partial / merge pair, the KV
+ * append and the promotion below.
  */
 va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
                           const void* k_scale, const void* v_scale, const int32_t* block_table,
                           const int32_t* ctx_lens, const int32_t* parent, int32_t num_splits,
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * Ragged rows: one call that mixes paged prefill segments, ordinary direct
+ * rows and draft trees (page "perf(qwen35): retain speculation during paged
+ * prefill", Mechanism: a step lowers [prefill segments][direct rows][tree
+ * rows] together, prefill and direct rows being positioned causal reads and
+ * parent metadata covering only the tree; Correctness failure found during
+ * qualification: the rows of one sequence must not change when other rows
+ * join the call).  Needs a plan with max_total_rows > 0.
+ *   cu_rows  [num_seqs + 1] int32, device: sequence s owns the packed rows
+ *            cu_rows[s] .. cu_rows[s+1] - 1 of q / out / lse (cu_rows[0] = 0,
+ *            non-decreasing, counts <= rows_per_seq, cu_rows[num_seqs] <=
+ *            max_total_rows; a count of 0 is allowed).  Its n_s rows are the
+ *            last n_s tokens of its context: row i at slot ctx_s - n_s + i.
+ *   q, out   [cu_rows[num_seqs], H, D] packed rows; lse [cu_rows[num_seqs], H]
+ *   parent   NULL (every row causal) or [cu_rows[num_seqs]] int32 packed the
+ *            same way with sequence-local values in [-1, i).  A sequence with
+ *            more than 64 rows must be a chain (parent[i] == i - 1).
+ * Every other argument as for verify_attn_run.  A sequence's outputs depend
+ * only on its own rows, context and pages and on the plan and num_splits.
+ * A bad cu_rows entry sets VA_FLAG_BAD_ROWS; that sequence writes nothing
+ * (outputs of rows it would own are unspecified).  The grid is fixed by the
+ * plan, so the call can be captured in a graph with live cu_rows.
+ */
+va_status verify_attn_run_ragged(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                 const void* k_scale, const void* v_scale, const int32_t* block_table,
+                                 const int32_t* ctx_lens, const int32_t* cu_rows, const int32_t* parent,
+                                 int32_t num_splits, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * The two launches of verify_attn_run, callable separately (same arguments

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     VA_FLAG_BAD_PAGE,
     VA_FLAG_BAD_PARENT,
     VA_FLAG_BAD_PATH,
+    VA_FLAG_BAD_ROWS,
     VA_OK,
     Plan,
     VaPlanInfo,
@@ -35,5 +36,6 @@ from ._binding import (  # noqa: F401
     verify_attn_run,
     verify_attn_run_merge,
     verify_attn_run_partial,
+    verify_attn_run_ragged,
     verify_attn_status_string,
 )

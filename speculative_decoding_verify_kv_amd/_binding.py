@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libverify_attn.so")
 
 VA_OK, VA_EINVAL, VA_EUNSUPPORTED, VA_EWORKSPACE, VA_EHIP = 0, -1, -2, -3, -4
 VA_F32, VA_F16, VA_BF16, VA_Q8_0 = 0, 1, 2, 3
-VA_FLAG_BAD_CTX, VA_FLAG_BAD_PAGE, VA_FLAG_BAD_PARENT, VA_FLAG_BAD_PATH = 0x1, 0x2, 0x4, 0x8
+VA_FLAG_BAD_CTX, VA_FLAG_BAD_PAGE, VA_FLAG_BAD_PARENT, VA_FLAG_BAD_PATH, VA_FLAG_BAD_ROWS = 0x1, 0x2, 0x4, 0x8, 0x10
 
 DTYPE_CODES = {"f32": VA_F32, "f16": VA_F16, "bf16": VA_BF16, "q8_0": VA_Q8_0}
 
@@ -38,6 +38,7 @@ class VaProblem(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("has_parent", ctypes.c_int32),
+        ("max_total_rows", ctypes.c_int32),
     ]
 
 
@@ -62,7 +63,8 @@ class VerifyAttnError(RuntimeError):
 _lib = None
 EXPORTED = (
     "verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_plan_destroy",
-    "verify_attn_run", "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv",
+    "verify_attn_run", "verify_attn_run_ragged", "verify_attn_run_partial", "verify_attn_run_merge",
+    "verify_attn_append_kv",
     "verify_attn_promote_kv", "verify_attn_promote_workspace_bytes", "verify_attn_read_flags",
     "verify_attn_status_string",
 )
@@ -88,6 +90,8 @@ def load(path: Optional[str] = None):
     lib.verify_attn_plan_destroy.restype = None
     run_args = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_run.argtypes = run_args
+    lib.verify_attn_run_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, ctypes.c_size_t,
+                                           vp]
     lib.verify_attn_run_partial.argtypes = run_args
     lib.verify_attn_run_merge.argtypes = [vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_append_kv.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -98,6 +102,7 @@ def load(path: Optional[str] = None):
     lib.verify_attn_status_string.argtypes = [i32]
     lib.verify_attn_status_string.restype = ctypes.c_char_p
     for n in ("verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_run",
+              "verify_attn_run_ragged",
               "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv", "verify_attn_promote_kv",
               "verify_attn_read_flags"):
         getattr(lib, n).restype = i32
@@ -117,12 +122,12 @@ def _check(st: int, what: str):
 
 def make_problem(*, num_seqs, rows_per_seq, num_q_heads, num_kv_heads, head_dim, num_pages, max_pages_per_seq,
                  max_ctx, q_dtype="bf16", kv_dtype="q8_0", out_dtype="f16", scale=0.0, has_parent=False,
-                 page_size=16) -> VaProblem:
+                 page_size=16, max_total_rows=0) -> VaProblem:
     return VaProblem(num_seqs=num_seqs, rows_per_seq=rows_per_seq, num_q_heads=num_q_heads,
                      num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size, num_pages=num_pages,
                      max_pages_per_seq=max_pages_per_seq, max_ctx=max_ctx, q_dtype=DTYPE_CODES[q_dtype],
                      kv_dtype=DTYPE_CODES[kv_dtype], out_dtype=DTYPE_CODES[out_dtype], scale=float(scale),
-                     has_parent=int(bool(has_parent)))
+                     has_parent=int(bool(has_parent)), max_total_rows=int(max_total_rows))
 
 
 class Plan:
@@ -191,6 +196,18 @@ def verify_attn_run(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table
                                 _ptr(lse), _ptr(workspace), wsb, _stream(stream))
     if raise_on_error:
         _check(st, "verify_attn_run")
+    return st
+
+
+def verify_attn_run_ragged(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, cu_rows, parent,
+                           num_splits, out, lse, workspace, workspace_bytes=None, stream=None, *,
+                           raise_on_error=True) -> int:
+    wsb = plan.workspace_bytes if workspace_bytes is None else int(workspace_bytes)
+    st = load().verify_attn_run_ragged(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                       _ptr(v_scale), _ptr(block_table), _ptr(ctx_lens), _ptr(cu_rows), _ptr(parent),
+                                       int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), wsb, _stream(stream))
+    if raise_on_error:
+        _check(st, "verify_attn_run_ragged")
     return st
 
 

@@ -21,13 +21,21 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool ragged(const va_problem& p) { return p.max_total_rows > 0; }
+
+// Packed query rows the plan holds: num_seqs * B, or max_total_rows (ragged).
+int64_t rows_capacity(const va_problem& p) {
+  return ragged(p) ? (int64_t)p.max_total_rows : (int64_t)p.num_seqs * p.rows_per_seq;
+}
+
 va_status check_problem(const va_problem* p) {
   if (!p) return VA_EINVAL;
   if (p->num_seqs < 1 || p->rows_per_seq < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
-      p->num_pages < 1 || p->max_pages_per_seq < 1 || p->max_ctx < 1)
+      p->num_pages < 1 || p->max_pages_per_seq < 1 || p->max_ctx < 1 || p->max_total_rows < 0)
     return VA_EINVAL;
   if (p->num_q_heads % p->num_kv_heads) return VA_EINVAL;
-  if (p->rows_per_seq > va::kMaxRows) return VA_EUNSUPPORTED;
+  if (p->rows_per_seq > (ragged(*p) ? va::kMaxRowsRagged : va::kMaxRows)) return VA_EUNSUPPORTED;
+  if (ragged(*p) && (int64_t)p->max_total_rows > (int64_t)p->num_seqs * p->rows_per_seq) return VA_EINVAL;
   if (p->page_size != va::kPage) return VA_EUNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return VA_EUNSUPPORTED;
   if (p->q_dtype != VA_F32 && p->q_dtype != VA_F16 && p->q_dtype != VA_BF16) return VA_EUNSUPPORTED;
@@ -37,7 +45,7 @@ va_status check_problem(const va_problem* p) {
   if (!(p->scale >= 0.f) || isinf(p->scale)) return VA_EINVAL;  // negative or NaN
   if (p->max_ctx < p->rows_per_seq) return VA_EINVAL;
   if ((int64_t)p->max_ctx > (int64_t)p->max_pages_per_seq * va::kPage) return VA_EINVAL;
-  if ((int64_t)p->num_seqs * p->rows_per_seq * p->num_q_heads > INT32_MAX) return VA_EUNSUPPORTED;
+  if (rows_capacity(*p) * p->num_q_heads > INT32_MAX) return VA_EUNSUPPORTED;
   return VA_OK;
 }
 
@@ -59,7 +67,7 @@ int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
   const int64_t npages = ceil_div(p.max_ctx, va::kPage);
   const int64_t s_pages = npages / 8;
   if (S > s_pages) S = s_pages;
-  const int64_t nrows = (int64_t)p.num_seqs * p.rows_per_seq * p.num_q_heads;
+  const int64_t nrows = rows_capacity(p) * p.num_q_heads;
   const double part_per_split = (double)nrows * (p.head_dim + 2) * 4.0;
   const double kv = (double)p.num_seqs * p.max_ctx * p.num_kv_heads * kv_bytes_per_token_head(p);
   const int64_t s_bytes = (int64_t)(0.5 * kv / part_per_split);
@@ -70,7 +78,7 @@ int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
 }
 
 size_t workspace_for(const va_problem& p, int S) {
-  const size_t nrows = (size_t)p.num_seqs * p.rows_per_seq * p.num_q_heads;
+  const size_t nrows = (size_t)rows_capacity(p) * p.num_q_heads;
   if (S <= 1) return va::kHeaderBytes;
   return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float);
 }
@@ -109,6 +117,7 @@ struct RunArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   const int32_t* parent;
+  const int32_t* cu_rows;  // ragged plans only
 };
 
 va_status check_run(const va_plan* plan, const RunArgs& a, int32_t num_splits, void* out, float* lse,
@@ -127,6 +136,8 @@ va_status check_run(const va_plan* plan, const RunArgs& a, int32_t num_splits, v
   }
   if ((p.has_parent != 0) != (a.parent != nullptr)) return VA_EINVAL;
   if (a.parent && !aligned(a.parent, 4)) return VA_EINVAL;
+  if (ragged(p) != (a.cu_rows != nullptr)) return VA_EINVAL;  // ragged plans run through verify_attn_run_ragged
+  if (a.cu_rows && !aligned(a.cu_rows, 4)) return VA_EINVAL;
   const int32_t S = num_splits ? num_splits : plan->num_splits;
   if (S < 1) return VA_EINVAL;
   if (S > plan->max_splits) return VA_EWORKSPACE;
@@ -148,9 +159,10 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
   pp.block_table = a.block_table;
   pp.ctx_lens = a.ctx_lens;
   pp.parent = a.parent;
+  pp.cu_rows = a.cu_rows;
   pp.out = out;
   pp.lse = lse;
-  const int64_t nrows = (int64_t)p.num_seqs * p.rows_per_seq * p.num_q_heads;
+  const int64_t nrows = rows_capacity(p) * p.num_q_heads;
   char* ws = static_cast<char*>(workspace);
   pp.flags = reinterpret_cast<uint32_t*>(ws);
   float* part = reinterpret_cast<float*>(ws + va::kHeaderBytes);
@@ -159,6 +171,7 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
   pp.part_l = pp.part_m + (int64_t)plan->max_splits * nrows;
   pp.num_seqs = p.num_seqs;
   pp.B = p.rows_per_seq;
+  pp.total_rows = (int32_t)rows_capacity(p);
   pp.H = p.num_q_heads;
   pp.KVH = p.num_kv_heads;
   pp.G = p.num_q_heads / p.num_kv_heads;
@@ -184,6 +197,8 @@ va::MergeParams merge_params(const va::PartialParams& pp, void* out, float* lse)
   mp.part_l = pp.part_l;
   mp.out = out;
   mp.lse = lse;
+  mp.live_rows = pp.cu_rows ? pp.cu_rows + pp.num_seqs : nullptr;
+  mp.heads = pp.H;
   mp.S = pp.S;
   mp.D = pp.D;
   mp.out_dtype = pp.out_dtype;
@@ -230,7 +245,7 @@ va_status verify_attn_run_partial(const va_plan* plan, const void* q, const void
                                   const int32_t* block_table, const int32_t* ctx_lens,
                                   const int32_t* parent, int32_t num_splits, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent};
+  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, nullptr};
   int32_t S = 0;
   va_status st = check_run(plan, a, num_splits, out, lse, workspace, workspace_bytes, &S);
   if (st != VA_OK) return st;
@@ -244,12 +259,13 @@ va_status verify_attn_run_partial(const va_plan* plan, const void* q, const void
 va_status verify_attn_run_merge(const va_plan* plan, int32_t num_splits, void* out, float* lse,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || !out || !workspace) return VA_EINVAL;
+  if (ragged(plan->prob)) return VA_EINVAL;  // the live row count comes with verify_attn_run_ragged
   if (!aligned(out, 16) || !aligned(workspace, 256) || (lse && !aligned(lse, 4))) return VA_EINVAL;
   const int32_t S = num_splits ? num_splits : plan->num_splits;
   if (S < 2) return VA_EINVAL;
   if (S > plan->max_splits || workspace_bytes < plan->workspace_bytes) return VA_EWORKSPACE;
   // Only the workspace layout and the output are needed.
-  const RunArgs none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const RunArgs none{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   const va::PartialParams pp = partial_params(plan, none, S, out, lse, workspace);
   if (va::launch_merge(merge_params(pp, out, lse), static_cast<hipStream_t>(stream)) != hipSuccess)
     return VA_EHIP;
@@ -261,7 +277,24 @@ va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool
                           const int32_t* ctx_lens, const int32_t* parent, int32_t num_splits,
                           void* out, float* lse, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent};
+  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, nullptr};
+  int32_t S = 0;
+  va_status st = check_run(plan, a, num_splits, out, lse, workspace, workspace_bytes, &S);
+  if (st != VA_OK) return st;
+  const va::PartialParams pp = partial_params(plan, a, S, out, lse, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (va::launch_partial(pp, plan->prob.kv_dtype, plan->tiling.nt, s) != hipSuccess) return VA_EHIP;
+  if (S > 1 && va::launch_merge(merge_params(pp, out, lse), s) != hipSuccess) return VA_EHIP;
+  return VA_OK;
+}
+
+va_status verify_attn_run_ragged(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                 const void* k_scale, const void* v_scale, const int32_t* block_table,
+                                 const int32_t* ctx_lens, const int32_t* cu_rows, const int32_t* parent,
+                                 int32_t num_splits, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!plan || !cu_rows) return VA_EINVAL;
+  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, cu_rows};
   int32_t S = 0;
   va_status st = check_run(plan, a, num_splits, out, lse, workspace, workspace_bytes, &S);
   if (st != VA_OK) return st;
@@ -276,7 +309,7 @@ va_status verify_attn_append_kv(const va_plan* plan, const void* k_new, const vo
                                 void* k_pool, void* v_pool, void* k_scale, void* v_scale,
                                 const int32_t* block_table, const int32_t* ctx_lens, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  if (!plan) return VA_EINVAL;
+  if (!plan || ragged(plan->prob)) return VA_EINVAL;  // B drafted rows per sequence only
   const va_problem& p = plan->prob;
   if (new_dtype != VA_F32 && new_dtype != VA_F16 && new_dtype != VA_BF16) return VA_EINVAL;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !ctx_lens || !workspace) return VA_EINVAL;
@@ -324,7 +357,7 @@ va_status verify_attn_promote_kv(const va_plan* plan, const int32_t* accepted, c
                                  const int32_t* parent, void* k_pool, void* v_pool, void* k_scale, void* v_scale,
                                  const int32_t* block_table, const int32_t* ctx_lens, int32_t* new_ctx,
                                  void* workspace, size_t workspace_bytes, void* stream) {
-  if (!plan) return VA_EINVAL;
+  if (!plan || ragged(plan->prob)) return VA_EINVAL;  // B drafted rows per sequence only
   const va_problem& p = plan->prob;
   if (!accepted || !n_accepted || !k_pool || !v_pool || !block_table || !ctx_lens || !workspace) return VA_EINVAL;
   if (!aligned(accepted, 4) || !aligned(n_accepted, 4) || (parent && !aligned(parent, 4)) ||

@@ -12,7 +12,8 @@ namespace va {
 
 constexpr int kPage = 16;
 constexpr int kMaxSplits = 256;
-constexpr int kMaxRows = 64;         // B limit (ancestry bitmask width)
+constexpr int kMaxRows = 64;         // B limit of a uniform plan (ancestry bitmask width)
+constexpr int kMaxRowsRagged = 4096; // per-sequence row limit of a ragged plan (chains past 64)
 constexpr size_t kHeaderBytes = 256; // workspace flag header
 
 // Kernel-side dtype codes (same values as va_dtype).
@@ -28,13 +29,15 @@ struct PartialParams {
   const int32_t* block_table;
   const int32_t* ctx_lens;
   const int32_t* parent;  // NULL => chain
+  const int32_t* cu_rows; // NULL => B rows per sequence; else [num_seqs + 1] packed row offsets
   void* out;              // direct mode output
   float* lse;             // direct mode lse (may be NULL)
   float* part_o;          // [S][nrows][D]
   float* part_m;          // [S][nrows]  (log2 units)
   float* part_l;          // [S][nrows]
   uint32_t* flags;
-  int32_t num_seqs, B, H, KVH, G, D;
+  int32_t num_seqs, B, H, KVH, G, D;  // B: rows per sequence (ragged: the largest count)
+  int32_t total_rows;     // ragged: capacity of the packed rows
   int32_t num_pages, max_pages, max_ctx;
   int32_t S;              // splits in this launch
   int32_t row_groups;     // workgroups along the B*G rows of one KV head
@@ -51,6 +54,8 @@ struct MergeParams {
   const float* part_l;
   void* out;
   float* lse;
+  const int32_t* live_rows; // ragged: &cu_rows[num_seqs]; rows from live_rows[0] * heads on are skipped
+  int32_t heads;
   int32_t S, D, out_dtype;
   int64_t nrows;
 };

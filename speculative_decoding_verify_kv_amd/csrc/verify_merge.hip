@@ -57,6 +57,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   typedef typename VecT<E>::type vec;
   __shared__ float red[kMergeWaves][D];
   const int64_t R = blockIdx.x;
+  if (p.live_rows && R >= (int64_t)p.live_rows[0] * p.heads) return;  // past the packed rows in use
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = p.S;

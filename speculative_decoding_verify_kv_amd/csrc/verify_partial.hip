@@ -169,7 +169,7 @@ struct Lay {
   using G = Geo<D, KVT>;
   static constexpr int P_BUF = 2 * NT * 1024;  // one tile's P: [h][nt][lane] x 16 B
   static constexpr int EX_BYTES = 2 * 16 * NT * 4;
-  static constexpr int MISC = 512 + 512 + EX_BYTES + 16;
+  static constexpr int MISC = 512 + 512 + EX_BYTES + 64;
   static constexpr int BUDGET = 160 * 1024;
   static constexpr int AVAIL = BUDGET - 2 * P_BUF - MISC;
   // deepest K / V rings that fit (V is consumed one iteration after K)
@@ -187,8 +187,8 @@ struct Lay {
   static constexpr int IDS_OFF = P_OFF + 2 * P_BUF;  // int32 [2][64] page ids
   static constexpr int ANC_OFF = IDS_OFF + 512;      // uint64 [64] ancestry masks
   static constexpr int EX_OFF = ANC_OFF + 512;       // float [2][16 NT] row exchange
-  static constexpr int FLAG_OFF = EX_OFF + EX_BYTES; // int flags [3]
-  static constexpr int BYTES = FLAG_OFF + 16;
+  static constexpr int FLAG_OFF = EX_OFF + EX_BYTES; // int flags [16]: [0..2] shared, [8..15] one per wave
+  static constexpr int BYTES = FLAG_OFF + 64;
   // Q staging (fp16 [16 NT][D]) during the prologue: the V ring receives
   // nothing before the first iteration.
   static constexpr int QST_BYTES = 16 * NT * D * 2;
@@ -292,9 +292,25 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     split = blockIdx.x % p.S;
     rg = blockIdx.x / p.S;
   }
-  const int B = p.B;
+  // Rows of this sequence: B each, or (ragged) cu_rows[s] .. cu_rows[s+1]
+  // of the packed q / out rows.  Row r of the group list is (head hl, row b)
+  // with r = hl * B + b.
+  int B = p.B;
+  int64_t r0 = (int64_t)s * p.B;
+  bool bad_rows = false;
+  if (p.cu_rows) {
+    const int a = p.cu_rows[s], e = p.cu_rows[s + 1];
+    bad_rows = a < 0 || e < a || e > p.total_rows || e - a > p.B;
+    B = bad_rows ? 0 : e - a;
+    r0 = a;
+  }
   const int M = B * p.G;
   const int rowbase = rg * QROWS;
+  if (rowbase >= M) {
+    // no rows of this sequence in this group (nothing is written)
+    if (bad_rows && tid == 0 && blockIdx.x == 0 && kvh == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_ROWS);
+    return;
+  }
 
   const int32_t* bt_row = p.block_table + (int64_t)s * p.max_pages;
 
@@ -322,13 +338,20 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     const int r = rowbase + rr;
     if (rr < QROWS && r < M) {
       const int hl = r / B, b = r % B;
-      const int64_t qrow = ((int64_t)(s * B + b) * p.H + kvh * p.G + hl) * D;
+      const int64_t qrow = ((r0 + b) * p.H + kvh * p.G + hl) * D;
       const char* src = reinterpret_cast<const char*>(p.q) + (qrow + (int64_t)c * (qf32 ? 4 : 8)) * (qf32 ? 4 : 2);
       qraw[u] = *reinterpret_cast<const u32x4*>(src);
     }
   }
   int par = 0;
-  if (p.parent && lane < B) par = p.parent[(int64_t)s * B + lane];
+  if (p.parent && lane < B) par = p.parent[r0 + lane];
+  // The ancestry bitmask covers 64 rows: a longer sequence (a ragged prefill
+  // segment) is a positioned causal chain, and a supplied parent array must
+  // say so (parent[i] == i - 1 for every row).
+  const bool long_rows = B > 64;
+  bool chain_bad = false;
+  if (long_rows && p.parent)
+    for (int i = tid; i < B; i += kBlockThreads) chain_bad |= p.parent[r0 + i] != i - 1;
 
   // ---- validate sequence metadata (device-resident) ----
   bool poison = false;
@@ -348,11 +371,20 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   }
   const int base = ctx - B;  // slot of drafted row 0
 
-  // ---- this split's pages and tiles of 4 pages ----
+  // Last key any row of this group can see: row b sees no slot past base + b.
+  const int rend = min(rowbase + QROWS, M);
+  int bmax = B - 1;
+  if (rend - rowbase < B) {
+    const int b0 = rowbase % B, b1 = (rend - 1) % B;
+    if (b1 >= b0) bmax = b1;
+  }
+  const int vis_pages = (base + bmax + 1 + kPage - 1) / kPage;
+
+  // ---- this split's pages (cut at the group's last visible key) and tiles of 4 pages ----
   const int npages = (ctx + kPage - 1) / kPage;
   const int pps = (npages + p.S - 1) / p.S;
   const int p_begin = min(split * pps, npages);
-  const int p_end = min(p_begin + pps, npages);
+  const int p_end = max(p_begin, min(min(p_begin + pps, npages), vis_pages));
   const int npg = p_end - p_begin;
   const int T = (npg + 3) >> 2;
   const int split_end = min(ctx, p_end * kPage);
@@ -392,12 +424,17 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         pr = pp;
       }
     }
-    if (lane < B) anc_lds[lane] = poison ? 0 : a;
+    // (a sequence past 64 rows is a chain: its rows are limited by position alone)
+    if (lane < B) anc_lds[lane] = poison ? 0 : long_rows ? ~(uint64_t)0 : a;
   }
   if (tid == 0) {
     flag_ref(0) = 0;
     flag_ref(1) = 0;
     flag_ref(2) = 0;
+  }
+  if (long_rows && p.parent) {
+    const bool wbad = __builtin_amdgcn_ballot_w64(chain_bad) != 0;
+    if (lane == 0) flag_ref(8 + wave) = wbad ? 1 : 0;
   }
   h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
 #pragma unroll
@@ -426,6 +463,15 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     }
   }
   __syncthreads();
+  if (long_rows && p.parent) {
+    bool bad = false;
+#pragma unroll
+    for (int w = 0; w < kBlockThreads / 64; ++w) bad |= flag_set(8 + w);
+    if (bad) {
+      poison = true;
+      flagbits |= VA_FLAG_BAD_PARENT;
+    }
+  }
 
   // ---- DMA issue ----
   const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * G::KPAGE;
@@ -533,11 +579,13 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       if constexpr (!decltype(mk)::value) {
         return z;
       } else {
+        // the prefix plus the row's ancestors (all earlier rows of a chain),
+        // never a slot past the row's own
         const int j = tile_tok0 + 16 * (2 * kh + u) + 4 * g4 + i;
-        const uint64_t anc = anc_lds[brow[nt]];
+        const uint64_t anc = anc_lds[brow[nt] & 63];
         const uint32_t rel = (uint32_t)(j - base) & 63u;
         const uint32_t bit = (uint32_t)(anc >> rel) & 1u;
-        const uint32_t vis = (uint32_t)(j < split_end) & ((uint32_t)(j < base) | bit);
+        const uint32_t vis = (uint32_t)(j < split_end) & (uint32_t)(j - base <= brow[nt]) & ((uint32_t)(j < base) | bit);
         return vis ? z : -INFINITY;
       }
     };
@@ -795,7 +843,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       if (r >= M) continue;
       const float Lrow = ex_lds[16 * nt + n16] + ex_lds[QROWS + 16 * nt + n16];
       const int hl = r / B, b = r % B;
-      const int64_t Rg = (int64_t)(s * B + b) * p.H + kvh * p.G + hl;
+      const int64_t Rg = (r0 + b) * p.H + kvh * p.G + hl;
       if (p.direct) {
         const float inv = any_poison ? __builtin_nanf("") : 1.0f / Lrow;
 #pragma unroll

@@ -1,0 +1,226 @@
+"""GPU parity of ragged rows (verify_attn_run_ragged): paged prefill segments,
+direct rows and a draft tree in one call, against the fp64 oracle.
+
+Source: the page "perf(qwen35): retain speculation during paged prefill",
+Mechanism (one step lowers [prefill segments][direct rows][tree rows]) and
+Correctness failure found during qualification (rows of one sequence changed
+when a tree suffix joined the launch at the 1,024-token boundary).  Every
+call goes through the C ABI; expected values come from the oracle only.
+"""
+
+import copy
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+import speculative_decoding_verify_kv_amd as va
+from speculative_decoding_verify_kv_amd import device as vdev
+
+from .gpu_util import check_parity, ensure_lib, errors, say
+from .test_oracle_ragged import tiny_ragged
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_lib()
+
+
+def run_ragged(w, num_splits=0, out_dtype="f16", *, plan=None, dev=None, cu_rows=None, q=None, parent=None):
+    """verify_attn_run_ragged on w (cu_rows / q / parent override the workload's);
+    returns (out fp64 [rows], lse fp64 [rows], flags, plan)."""
+    import torch
+
+    dev = dev if dev is not None else vdev.to_device(w)
+    if plan is None:
+        plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype=out_dtype), num_splits, 0)
+    cap = plan.problem.max_total_rows
+    ws = vdev.workspace(plan)
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[out_dtype]
+    out = torch.full((cap, w.H, w.D), float("nan"), dtype=dt, device="cuda")
+    lse = torch.full((cap, w.H), float("nan"), dtype=torch.float32, device="cuda")
+    cu = dev["cu_rows"] if cu_rows is None else torch.from_numpy(np.asarray(cu_rows, np.int32)).cuda()
+    qq = dev["q"] if q is None else q
+    par = dev["parent"] if parent is None else parent
+    va.verify_attn_run_ragged(plan, qq, dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                              dev["block_table"], dev["ctx_lens"], cu, par, num_splits, out, lse, ws)
+    torch.cuda.synchronize()
+    flags = va.verify_attn_read_flags(plan, ws)
+    return out.float().cpu().double().numpy(), lse.cpu().double().numpy(), flags, plan
+
+
+_cache = {}
+
+
+def mixed():
+    if "mixed" not in _cache:
+        w = S.mixed_lowering()
+        say(f"[oracle] {w.name} rows={w.cu_rows.tolist()} ctx={w.ctx_lens.tolist()}")
+        o, l = oracle.attention(w)
+        _cache["mixed"] = (w, o, l)
+    return _cache["mixed"]
+
+
+@pytest.mark.parametrize("S_", [1, 8, 0])
+def test_mixed_lowering(S_):
+    w, ref, lref = mixed()
+    say(f"[case] mixed lowering S={S_}")
+    got, lse, flags, plan = run_ragged(w, S_, "f16")
+    n = w.total_rows
+    assert flags == 0
+    check_parity(got[:n], ref, "f16", f"mixed S={plan.info().num_splits if S_ == 0 else S_}")
+    assert np.abs(lse[:n] - lref).max() <= 2e-3
+    assert np.all(np.isnan(got[n:]))  # nothing past the packed rows is written
+
+
+@pytest.mark.parametrize("kv,S_", [("f16", 1), ("f16", 3), ("q8_0", 1), ("q8_0", 4)])
+def test_tiny_ragged(kv, S_):
+    # an empty sequence, one direct row, a 70-row chain (past the 64-row
+    # ancestry window) and a tree; D=64, 4 query heads over 2 KV heads
+    w = tiny_ragged(kv)
+    say(f"[case] tiny ragged kv={kv} S={S_} rows={np.diff(w.cu_rows).tolist()}")
+    ref, lref = oracle.attention(w)
+    got, lse, flags, _ = run_ragged(w, S_, "f32")
+    assert flags == 0
+    check_parity(got[:w.total_rows], ref, "f32", f"tiny ragged {kv} S={S_}")
+    assert np.abs(lse[:w.total_rows] - lref).max() <= 2e-3
+
+
+@pytest.mark.parametrize("S_", [1, 8, 0])
+def test_long_prefill_segment(S_):
+    # 300 prefill rows ending at ctx 1500 plus one direct row: many row groups,
+    # each cut at its last visible key
+    if "prefill" not in _cache:
+        w = S.make_workload("prefill300", ctx_lens=[1500, 2100], rows=[300, 1], H=24, KVH=4, D=256,
+                            q_dtype="bf16", kv_dtype="q8_0", seed=51, permute=True, spare_pages=7, poison=True)
+        say("[oracle] prefill300")
+        _cache["prefill"] = (w, oracle.attention(w)[0])
+    w, ref = _cache["prefill"]
+    say(f"[case] long prefill S={S_}")
+    got, _, flags, plan = run_ragged(w, S_, "f16")
+    assert flags == 0
+    say(f"  plan: S={plan.info().num_splits} row_groups={plan.info().row_groups}")
+    check_parity(got[:w.total_rows], ref, "f16", f"prefill300 S={S_}")
+
+
+@pytest.mark.parametrize("S_", [1, 8])
+def test_uniform_rows_through_ragged_entry_bitwise(S_):
+    # B rows per sequence written as cu_rows = [0, B, 2B, ...]: the same plan
+    # shape and split count must give the same bits as verify_attn_run
+    import torch
+
+    w = S.paged_ragged(ctxs=(1016, 1024, 1032, 3000))
+    wr = copy.deepcopy(w)
+    wr.cu_rows = np.arange(0, w.num_seqs * w.B + 1, w.B, dtype=np.int32)
+    say(f"[case] uniform via ragged S={S_}")
+    dev = vdev.to_device(wr)
+    plan_u = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f32"), S_, 0)
+    ws = vdev.workspace(plan_u)
+    out_u, lse_u = vdev.empty_out(w, "f32")
+    va.verify_attn_run(plan_u, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                       dev["block_table"], dev["ctx_lens"], None, S_, out_u, lse_u, ws)
+    torch.cuda.synchronize()
+    got, lse, flags, plan_r = run_ragged(wr, S_, "f32", dev=dev)
+    assert plan_r.info().rows_per_group == plan_u.info().rows_per_group
+    assert flags == 0
+    np.testing.assert_array_equal(got, out_u.double().cpu().numpy())
+    np.testing.assert_array_equal(lse, lse_u.double().cpu().numpy())
+
+
+@pytest.mark.parametrize("S_", [8, 0])
+def test_rows_joining_do_not_change_other_rows_bitwise(S_):
+    """The tree sequence joining the call, or the prefill segments leaving it,
+    leaves every other sequence's rows bit for bit unchanged (one plan)."""
+    import torch
+
+    w, ref, _ = mixed()
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f16"), S_, 0)
+    full, _, flags, _ = run_ragged(w, S_, "f16", plan=plan, dev=dev)
+    assert flags == 0
+    cu = w.cu_rows
+    # 1) the tree sequence with no rows
+    no_tree = cu.copy()
+    no_tree[-1] = no_tree[-2]
+    a, _, flags, _ = run_ragged(w, S_, "f16", plan=plan, dev=dev, cu_rows=no_tree)
+    assert flags == 0
+    np.testing.assert_array_equal(a[:cu[-2]], full[:cu[-2]])
+    # 2) the prefill segments with no rows: the direct and tree rows move to the
+    #    front of the packed layout and keep their bits
+    keep = cu[2]
+    cu2 = np.concatenate([[0, 0, 0], cu[3:] - keep]).astype(np.int32)
+    q2 = dev["q"][keep:].contiguous()
+    par2 = dev["parent"][keep:].contiguous()
+    b, _, flags, _ = run_ragged(w, S_, "f16", plan=plan, dev=dev, cu_rows=cu2, q=q2, parent=par2)
+    assert flags == 0
+    np.testing.assert_array_equal(b[:cu2[-1]], full[keep:cu[-1]])
+    del torch
+
+
+def test_bad_rows_and_long_non_chain_flagged():
+    w, ref, _ = mixed()
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f16"), 8, 0)
+    cu = w.cu_rows
+    # the last sequence claims rows past the packed capacity: flagged, nothing
+    # of it written, the others intact
+    bad = cu.copy()
+    bad[-1] = cu[-1] + 5
+    say("[case] cu_rows past capacity")
+    got, _, flags, _ = run_ragged(w, 8, "f16", plan=plan, dev=dev, cu_rows=bad)
+    assert flags & va.VA_FLAG_BAD_ROWS
+    check_parity(got[:cu[-2]], ref[:cu[-2]], "f16", "others beside a bad cu_rows entry")
+    # a decreasing entry
+    bad = cu.copy()
+    bad[3] = cu[2] - 1
+    got, _, flags, _ = run_ragged(w, 8, "f16", plan=plan, dev=dev, cu_rows=bad)
+    assert flags & va.VA_FLAG_BAD_ROWS
+    check_parity(got[:cu[2] - 1], ref[:cu[2] - 1], "f16", "sequences before a decreasing cu_rows entry")
+    # the 100-row prefill segment with a parent that is not a chain: its rows NaN
+    wb = copy.deepcopy(w)
+    wb.parent = w.parent.copy()
+    wb.parent[77] = 10
+    say("[case] long segment with a non-chain parent")
+    got, _, flags, _ = run_ragged(wb, 8, "f16", plan=plan)
+    assert flags & va.VA_FLAG_BAD_PARENT
+    assert np.all(np.isnan(got[:100]))
+    check_parity(got[100:cu[-1]], ref[100:], "f16", "others beside a bad long parent")
+
+
+def test_ragged_graph_replay_with_live_rows():
+    """Capture one ragged call, then change cu_rows / ctx on the device and
+    replay: every replay matches the oracle for the rows it was given."""
+    import torch
+
+    w, ref, _ = mixed()
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f16"), 8, 0)
+    ws = vdev.workspace(plan)
+    cap = plan.problem.max_total_rows
+    out = torch.empty((cap, w.H, w.D), dtype=torch.float16, device="cuda")
+    lse = torch.empty((cap, w.H), dtype=torch.float32, device="cuda")
+    cu_live = dev["cu_rows"].clone()
+    s = torch.cuda.Stream()
+    args = lambda: (plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                    dev["block_table"], dev["ctx_lens"], cu_live, dev["parent"], 8, out, lse, ws)
+    with torch.cuda.stream(s):
+        va.verify_attn_run_ragged(*args(), stream=s)  # warm up outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        va.verify_attn_run_ragged(*args(), stream=s)
+    torch.cuda.synchronize()
+    cu = w.cu_rows
+    no_tree = cu.copy()
+    no_tree[-1] = no_tree[-2]
+    for rep, c in enumerate([cu, no_tree, cu]):
+        cu_live.copy_(torch.from_numpy(c.astype(np.int32)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().double().numpy()
+        n = int(c[-1])
+        check_parity(got[:n], ref[:n], "f16", f"graph replay {rep} rows={n}")

@@ -238,3 +238,56 @@ def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4):
         assert va.verify_attn_status_string(st)
     assert va.verify_attn_status_string(-99) == "unknown status"
+
+
+# ---------------------------------------------------------------------------
+# ragged plans (verify_attn_run_ragged)
+# ---------------------------------------------------------------------------
+
+def ragged_status(plan, **over):
+    a = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, k_scale=FAKE, v_scale=FAKE, block_table=FAKE, ctx_lens=FAKE,
+             cu_rows=FAKE, parent=None, num_splits=0, out=FAKE, lse=None, workspace=FAKE,
+             workspace_bytes=plan.workspace_bytes)
+    a.update(over)
+    return va.verify_attn_run_ragged(plan, a["q"], a["k_pool"], a["v_pool"], a["k_scale"], a["v_scale"],
+                                     a["block_table"], a["ctx_lens"], a["cu_rows"], a["parent"], a["num_splits"],
+                                     a["out"], a["lse"], a["workspace"], a["workspace_bytes"], None,
+                                     raise_on_error=False)
+
+
+def test_ragged_plan_sizes_by_packed_rows(lib):
+    # 5 sequences, at most 100 rows each, 149 packed rows: the workspace and the
+    # row tiling follow the packed capacity and the largest count
+    prob = qwen(num_seqs=5, rows_per_seq=100, max_total_rows=149, max_ctx=40000, max_pages_per_seq=2500,
+                num_pages=8192)
+    plan = va.verify_attn_plan_for_cus(prob, 8, 256)
+    info = plan.info()
+    assert info.rows_per_group == 96 and info.row_groups == 7  # 600 rows -> 38 tiles -> 7 groups of 6
+    assert info.workspace_bytes == 256 + 8 * 149 * 24 * 258 * 4
+    # long prefill segments are allowed only in ragged plans
+    assert plan_status(qwen(rows_per_seq=65)) == va.VA_EUNSUPPORTED
+    assert plan_status(qwen(rows_per_seq=4096, max_total_rows=4096, max_ctx=32768)) == va.VA_OK
+    assert plan_status(qwen(rows_per_seq=4097, max_total_rows=4097, max_ctx=32768)) == va.VA_EUNSUPPORTED
+    # capacity above num_seqs * rows_per_seq, or negative
+    assert plan_status(qwen(num_seqs=2, rows_per_seq=10, max_total_rows=21)) == va.VA_EINVAL
+    assert plan_status(qwen(max_total_rows=-1)) == va.VA_EINVAL
+
+
+def test_ragged_entry_checks(lib):
+    ragged = va.verify_attn_plan_for_cus(qwen(num_seqs=3, rows_per_seq=40, max_total_rows=50), 4, 256)
+    uniform = va.verify_attn_plan_for_cus(qwen(), 4, 256)
+    assert ragged_status(uniform) == va.VA_EINVAL                 # uniform plans take verify_attn_run
+    assert ragged_status(ragged, cu_rows=None) == va.VA_EINVAL
+    assert ragged_status(ragged, cu_rows=FAKE + 2) == va.VA_EINVAL
+    assert ragged_status(ragged, parent=FAKE) == va.VA_EINVAL     # has_parent == 0
+    assert ragged_status(ragged, num_splits=5) == va.VA_EWORKSPACE
+    assert ragged_status(ragged, workspace_bytes=ragged.workspace_bytes - 1) == va.VA_EWORKSPACE
+    assert ragged_status(ragged, q=FAKE + 8) == va.VA_EINVAL
+    # the ragged plan is refused by every entry point that assumes B rows per sequence
+    assert run_status(ragged) == va.VA_EINVAL
+    f = va.verify_attn_run_merge
+    assert f(ragged, 4, FAKE, None, FAKE, ragged.workspace_bytes, None, raise_on_error=False) == va.VA_EINVAL
+    assert append_status(ragged) == va.VA_EINVAL
+    assert promote_status(ragged) == va.VA_EINVAL
+    assert va.load().verify_attn_run_ragged(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
+                                            None, FAKE, 1 << 30, None) == va.VA_EINVAL
