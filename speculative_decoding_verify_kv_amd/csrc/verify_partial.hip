@@ -66,7 +66,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRoleWaves = 4;                      // score waves; as many output waves
 constexpr int kBlockThreads = 64 * 2 * kRoleWaves;  // 512
-constexpr float kLazyRescale = 15.0f;  // 2^15 < 65504: the largest P value fp16 holds safely
+// A lane's partial row sum over its P values of a tile bounds each of them, so
+// sums at or below 2^15 keep every P value well inside fp16 (max 65504).
+constexpr float kLazyRescale = 32768.0f;
 constexpr float kFiniteFloor = -1e30f;  // stands for an unset (-inf) reference in differences
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -590,10 +592,10 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       }
     };
 
-    // P = 2^(z - m_ref) -> fp16 into the tile's P buffer; returns the largest
-    // exponent seen (for the overflow test) and leaves the row sums in lt.
+    // P = 2^(z - m_ref) -> fp16 into the tile's P buffer; leaves the lane's
+    // row sums in lt and returns the largest of them (the overflow test).
     auto write_p_t = [&](int j, auto mk) __attribute__((always_inline)) -> float {
-      float tmx = -INFINITY;
+      float lmx = 0.f;
       const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf + (g4 >> 1) * NT * 1024 + 8 * (g4 & 1);
 #pragma unroll
       for (int nt = 0; nt < NS; ++nt) {
@@ -607,7 +609,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
             float t;
             if constexpr (decltype(mk)::value) t = zval(u, nt, i, mk) - mre;
             else t = __builtin_fmaf(sacc[u][nt][i], c2, -mre);
-            tmx = fmaxf(tmx, t);
             pv[i] = fast_exp2(t);
             ls += pv[i];
           }
@@ -615,8 +616,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
           *LDS_PTR(h16x4, pb + (NS * rh + nt) * 1024 + (n16 + 16 * (2 * kh + u)) * 16) = ph;
         }
         lt[nt] = ls;
+        lmx = fmaxf(lmx, ls);
       }
-      return tmx;
+      return lmx;
     };
     auto write_p = [&](int j) __attribute__((always_inline)) -> float {
       return masked ? write_p_t(j, std::true_type{}) : write_p_t(j, std::false_type{});
@@ -665,12 +667,26 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
               sw[u][0] = *LDS_PTR(uint32_t, sp);
             }
           }
+          // the whole tile's K bytes for this wave in one burst of LDS reads,
+          // so one read latency is paid per tile rather than one per chunk
+          u32x4 raw_k[2][G::KCH];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int c = 0; c < G::KCH; ++c)
+              raw_k[u][c] = *LDS_PTR(u32x4, st + (2 * kh + u) * G::KPAGE + 1024 * c + 16 * lane);
+          // keep the burst together (the scheduler would otherwise sink each
+          // read next to its use and wait for it there)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int c = 0; c < G::KCH; ++c) asm volatile("" : "+v"(raw_k[u][c]));
           const uint32_t sel = (g4 >> 1) ? 0x03020302u : 0x01000100u;
 #pragma unroll
           for (int c = 0; c < G::KCH; ++c) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const u32x4 raw = *LDS_PTR(u32x4, st + (2 * kh + u) * G::KPAGE + 1024 * c + 16 * lane);
+              const u32x4 raw = raw_k[u][c];
               const h16x2 d2 = as_h2(__builtin_amdgcn_perm(sw[u][c], sw[u][c], sel));
               const h16x8 k0 = deq8(raw[0], raw[1], d2, d2, d2, d2);
               const h16x8 k1 = deq8(raw[2], raw[3], d2, d2, d2, d2);
@@ -693,8 +709,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
             }
           }
         }
-        const float tmx = write_p(j);
-        if (tmx > kLazyRescale) flag_ref(i & 1) = 1;
+        if (write_p(j) > kLazyRescale) flag_ref(i & 1) = 1;  // an unset reference gives +inf sums
       }
       // K of tile i + 1 (partly the partner wave's) must have landed before the barrier
       if (i + 1 < T) wait_vmcnt_n<NDMA>(min(T - 1, i + RK - 1) - (i + 1));
@@ -759,7 +774,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       if (i >= 1) {
         const int j = i - 1;
         const int tile_tok0 = (p_begin + 4 * j) * kPage;
-        const bool vtail = tile_tok0 + 64 > split_end;
+        const bool vtail = tile_tok0 + 64 > split_end;  // only a split's last tile
         const uint32_t st = lds0 + L::VR_OFF + (j % RV) * G::V_STAGE;
         const uint32_t pb = lds0 + L::P_OFF + (j & 1) * fbuf;
         h16x8 pf[2][NT];
@@ -769,16 +784,25 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
           for (int nt = 0; nt < NT; ++nt) pf[h][nt] = *LDS_PTR(h16x8, pb + (h * NT + nt) * 1024 + 16 * lane);
         const int tok_lane = tile_tok0 + 16 * g4;  // this lane's page starts here
         if constexpr (G::Q8) {
-          // scales of block bb, tokens 8h..8h+7 of page g: one 16-byte read
           constexpr int NB = (G::DO >= 32) ? G::DO / 32 : 1;  // scale blocks per output wave
+          const int bb0 = (role * G::DO) / 32;
+          if (vtail) {
+            // Slots at or past split_end may hold anything (NaN included):
+            // clear this wave's scales of them in the stage, so their V reads
+            // as 0.  Lane (g, m) owns slot m of page g; the wave reads only
+            // its own blocks, after these writes (LDS keeps one wave's order).
+            if (tile_tok0 + lane >= split_end)
+#pragma unroll
+              for (int b = 0; b < NB; ++b)
+                *LDS_PTR(uint16_t, st + 4 * G::VPAGE + g4 * D + (bb0 + b) * 32 + 2 * n16) = 0;
+          }
+          // scales of block bb, tokens 8h..8h+7 of page g: one 16-byte read
           h16x2 vs[NB][2][4];
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
-            const int bb = (role * G::DO) / 32 + b;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              u32x4 w = *LDS_PTR(u32x4, st + 4 * G::VPAGE + g4 * D + bb * 32 + 16 * h);
-              if (vtail) w &= tail_mask(tok_lane + 8 * h, split_end);
+              const u32x4 w = *LDS_PTR(u32x4, st + 4 * G::VPAGE + g4 * D + (bb0 + b) * 32 + 16 * h);
 #pragma unroll
               for (int e = 0; e < 4; ++e) vs[b][h][e] = as_h2(w[e]);
             }
