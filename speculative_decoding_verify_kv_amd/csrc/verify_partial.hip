@@ -411,7 +411,10 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     const bool spec_ok = (p_begin == pb_spec) && (npg <= pe_spec - pb_spec);
     ids_lds[tid] = (tid < npg) ? (spec_ok ? id_spec : bt_row[p_begin + tid]) : 0;
   }
-  if (wave == 0) {
+  if (wave == 0 && !p.parent) {
+    // chain: the positional limit alone decides
+    anc_lds[lane] = poison ? 0 : ~(uint64_t)0;
+  } else if (wave == 0) {
     // anc(i) = {i} + anc(parent[i]) by pointer jumping: after k rounds, a
     // holds the ancestors within distance 2^k and pr the one at distance 2^k.
     int pr = (lane < B && par < lane) ? par : -1;
