@@ -10,24 +10,26 @@
 //
 // The workgroup has 8 waves in two roles, one of each role per SIMD, so that
 // one wave's matrix-core work overlaps the other's vector work:
-//   score waves p = 0..3   each owns page p of every 64-key tile: LDS-DMA of
-//                          that page's K (and scales), int8 -> fp16 dequant,
+//   score waves (rh, kh)   rows half rh, pages 2kh and 2kh + 1 of every
+//                          64-key tile: int8 -> fp16 dequant of K from LDS,
 //                          S^T = K Q^T on v_mfma_f32_16x16x32_f16 (keys on M,
 //                          rows on N, Q resident in registers), causal / tree /
 //                          page-tail mask, P = 2^(t - m_ref) in fp16 -> LDS.
-//   output waves q = 0..3  each owns head_dim quarter q: LDS-DMA of that
-//                          quarter of the tile's V (and one page's scales),
-//                          dequant, O^T += V^T P^T on the same MFMA, with P of
-//                          the previous tile read from LDS.
+//   output waves q = 0..3  each owns head_dim quarter q: dequant of that
+//                          quarter of the tile's V, O^T += V^T P^T on the same
+//                          MFMA, with P of the previous tile read from LDS.
+//                          They also issue every LDS-DMA: page q of K (and its
+//                          scales), that quarter of V (and page q's scales).
 // Every KV element is therefore dequantised once per workgroup, and O lives
 // in exactly one wave, so the epilogue needs no cross-wave O reduction.
 //
 // Pipeline: separate K and V rings of R stages, filled by
 // global_load_lds_dwordx4 (no VGPR holds data in flight).  Iteration i: score
 // waves compute tile i while output waves accumulate tile i-1; one barrier per
-// iteration.  K of tile i + R - 1 and V of tile i + R - 2 are issued at the
-// start of iteration i, each wave issuing the same number of DMA instructions
-// and waiting only on its own vmcnt before the barrier.
+// iteration.  K of tile i + R_K - 1 and V of tile i + R_V - 2 are issued at the
+// start of iteration i by the output waves, which wait on their own vmcnt
+// before the barrier; the score waves, whose work bounds the loop, issue no
+// DMA and wait on nothing but the barrier.
 //
 // Softmax: log2 domain with a reference max per row held by every wave.  A
 // score may exceed its row's reference by at most 15 (P stays within fp16);
@@ -132,12 +134,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Wait until at most n * PER of this wave's vector-memory loads are in flight.
+// Wait until at most n * PER of this wave's vector-memory loads are in flight
+// (n is clamped to [0, 4]).
 template <int PER>
 __device__ __forceinline__ void wait_vmcnt_n(int n) {
   if (n <= 0) wait_vmcnt<0>();
   else if (n == 1) wait_vmcnt<PER>();
-  else wait_vmcnt<2 * PER>();
+  else if (n == 2) wait_vmcnt<2 * PER>();
+  else if (n == 3) wait_vmcnt<3 * PER>();
+  else wait_vmcnt<4 * PER>();
 }
 
 // Workgroup barrier that makes this wave's LDS writes visible; it does not
@@ -158,11 +163,11 @@ struct Geo {
   static constexpr int DO = D / 4;                // head_dim entries per output wave
   static constexpr int MTO = DO / 16;             // 16-dim tiles per output wave
   static constexpr int VCH = MTO * (VROW / 16);   // 1 KB V chunks per output wave per tile
-  static constexpr int NDMA = KCH + (Q8 ? 1 : 0); // DMA instructions per wave per tile
+  static constexpr int NDMA = KCH + (Q8 ? 1 : 0); // DMA instructions of one K page or V quarter of a tile
   static constexpr int K_STAGE = 4 * KPAGE + 4 * SPB;
   static constexpr int V_STAGE = 4 * VPAGE + 4 * SPB;
   static constexpr int KSTEPS = D / 32;
-  static_assert(KCH == VCH, "score and output waves issue the same number of DMAs");
+  static_assert(KCH == VCH, "a tile's K page and V quarter take the same number of DMAs");
   static_assert(KPAGE % 1024 == 0, "page must be whole KB");
 };
 
@@ -301,7 +306,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   int64_t r0 = (int64_t)s * p.B;
   bool bad_rows = false;
   if (p.cu_rows) {
-    const int a = p.cu_rows[s], e = p.cu_rows[s + 1];
+    const auto* cu = reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.cu_rows + s));
+    const int a = cu[0], e = cu[1];
     bad_rows = a < 0 || e < a || e > p.total_rows || e - a > p.B;
     B = bad_rows ? 0 : e - a;
     r0 = a;
@@ -320,7 +326,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // (1) ctx; (2) the block-table entries of this split as placed for
   // ctx = max_ctx (the usual case; checked below, reloaded otherwise);
   // (3) the group's Q rows as raw 16-byte units; (4) the parent array.
-  int ctx = p.ctx_lens[s];
+  // Uniform metadata is read through the scalar cache (it is never written
+  // while the kernel runs), so no vector wait sits in front of the loads below.
+  int ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s));
   const int npg_max = (p.max_ctx + kPage - 1) / kPage;
   const int pps_spec = (npg_max + p.S - 1) / p.S;
   const int pb_spec = min(split * pps_spec, npg_max);
@@ -329,20 +337,33 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   if (tid < 128 && pb_spec + tid < pe_spec) id_spec = bt_row[pb_spec + tid];
 
   const bool qf32 = p.q_dtype == kF32;
-  const int upr = qf32 ? D / 4 : D / 8;  // 16-byte Q units per row
+  const int upr = qf32 ? D / 4 : D / 8;  // 16-byte Q units per row (a power of two)
   constexpr int QU_MAX = (QROWS * (D / 4) + kBlockThreads - 1) / kBlockThreads;
   u32x4 qraw[QU_MAX];
+  {
+    // unit u of this thread is 16-byte column c of group row rr + u * step;
+    // row r = hl * B + b is stepped without a division per unit
+    const int step = kBlockThreads / upr;
+    const int c = tid & (upr - 1);
+    int rr = tid / upr;
+    int hl = (rowbase + rr) / B;
+    int b = rowbase + rr - hl * B;
+    const int dh = step / B, db = step - dh * B;
 #pragma unroll
-  for (int u = 0; u < QU_MAX; ++u) {
-    qraw[u] = u32x4{0u, 0u, 0u, 0u};
-    const int idx = tid + u * kBlockThreads;
-    const int rr = idx / upr, c = idx % upr;
-    const int r = rowbase + rr;
-    if (rr < QROWS && r < M) {
-      const int hl = r / B, b = r % B;
-      const int64_t qrow = ((r0 + b) * p.H + kvh * p.G + hl) * D;
-      const char* src = reinterpret_cast<const char*>(p.q) + (qrow + (int64_t)c * (qf32 ? 4 : 8)) * (qf32 ? 4 : 2);
-      qraw[u] = *reinterpret_cast<const u32x4*>(src);
+    for (int u = 0; u < QU_MAX; ++u) {
+      qraw[u] = u32x4{0u, 0u, 0u, 0u};
+      if (rr < QROWS && rowbase + rr < M) {
+        const int64_t qrow = ((r0 + b) * p.H + kvh * p.G + hl) * D;
+        const char* src = reinterpret_cast<const char*>(p.q) + (qrow + (int64_t)c * (qf32 ? 4 : 8)) * (qf32 ? 4 : 2);
+        qraw[u] = *reinterpret_cast<const u32x4*>(src);
+      }
+      rr += step;
+      hl += dh;
+      b += db;
+      if (b >= B) {
+        b -= B;
+        ++hl;
+      }
     }
   }
   int par = 0;
@@ -540,9 +561,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     // wave (rh, kh): rows [16 NS rh, 16 NS (rh + 1)) of the group, pages
     // 2kh and 2kh + 1 of every tile.
     const int rh = role & 1, kh = role >> 1;
-#pragma unroll
-    for (int j = 0; j < RK - 1; ++j)
-      if (j < T) issue_k(j);
 
     // Q fragments: k-step ks covers dims dim0(ks, g) + [0, 8) for lane group g.
     h16x8 qf[KSTEPS][NS];
@@ -560,10 +578,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       const int r = rowbase + rr;
       brow[nt] = (r < M) ? r % B : 0;
     }
-    // tile 0's K (R_K - 2 more tiles queued behind it) must have landed and
-    // be visible to the partner wave before the first iteration
-    if (T > 0) wait_vmcnt_n<NDMA>(min(T, RK - 1) - 1);
-    __syncthreads();
+    __syncthreads();  // tile 0's K has landed (the output waves waited for it)
 
     float mref[NS], lacc[NS], lt[NS];
     f32x4 sacc[2][NS];
@@ -637,13 +652,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     };
 
     for (int i = 0; i <= T; ++i) {
-      if (i + RK - 1 < T) issue_k(i + RK - 1);
-      if (wave == 0 && (i & 15) == 1 && i > 16) {
-        // page ids of chunk (i/16 + 1) into the buffer chunk i/16 - 1 used
-        const int chunk = (i >> 4) + 1;
-        const int off = 64 * chunk + lane;
-        if (off < npg) dma_saddr_b32(bt_row + p_begin + 64 * chunk, 4 * lane, lds0 + L::IDS_OFF + (chunk & 1) * 256);
-      }
       if (i < T) {
         const int j = i;
         tile_tok0 = (p_begin + 4 * j) * kPage;
@@ -714,8 +722,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         }
         if (write_p(j) > kLazyRescale) flag_ref(i & 1) = 1;  // an unset reference gives +inf sums
       }
-      // K of tile i + 1 (partly the partner wave's) must have landed before the barrier
-      if (i + 1 < T) wait_vmcnt_n<NDMA>(min(T - 1, i + RK - 1) - (i + 1));
       lds_barrier();
       if (flag_set(i & 1)) {
         // ---- rare path: raise the references (score side) ----
@@ -754,7 +760,29 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     __syncthreads();
   } else {
     // ========================= output waves =========================
+    // Output wave q issues every DMA of the loop: page q of each tile's K
+    // (and its scales) besides its quarter of V, so the score waves, which
+    // bound the loop, issue none.  The K ring is free from the start.
+#pragma unroll
+    for (int j = 0; j < RK - 1; ++j)
+      if (j < T) issue_k(j);
+    // tile 0's K must have landed before the score waves' first iteration
+    if (T > 0) wait_vmcnt_n<NDMA>(min(T, RK - 1) - 1);
     __syncthreads();  // matches the score waves' Q-fragment barrier
+
+    // DMA groups (one tile's K page or V quarter, NDMA instructions each) in
+    // issue order: K 0 .. RK-2 before the loop; at iteration t, K t+RK-1,
+    // then V 0 .. RV-2 (t = 0) or V t+RV-2 (t > 0), each while below T.
+    // ck(t) / cv(t): K / V groups issued through iteration t.
+    auto ck = [&](int t) __attribute__((always_inline)) { return min(T, RK + t); };
+    auto cv = [&](int t) __attribute__((always_inline)) { return t < 0 ? 0 : min(T, RV - 1 + t); };
+    // 1-based issue position of K j and of V j
+    auto pos_k = [&](int j) __attribute__((always_inline)) { return j <= RK - 2 ? j + 1 : ck(j - RK) + cv(j - RK) + 1; };
+    auto pos_v = [&](int j) __attribute__((always_inline)) {
+      if (j <= RV - 2) return ck(0) + j + 1;
+      const int t = j - RV + 2;
+      return ck(t) + cv(t - 1) + 1;
+    };
 
     f32x4 oacc[G::MTO][NT];
 #pragma unroll
@@ -766,6 +794,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     for (int nt = 0; nt < NT; ++nt) mref[nt] = -INFINITY;
 
     for (int i = 0; i <= T; ++i) {
+      if (i + RK - 1 < T) issue_k(i + RK - 1);
       if (i == 0) {
         // the V ring held the Q staging until the barrier above
 #pragma unroll
@@ -773,6 +802,12 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
           if (j < T) issue_v(j);
       } else if (i + RV - 2 < T) {
         issue_v(i + RV - 2);
+      }
+      if (wave == kRoleWaves && (i & 15) == 1 && i > 16) {
+        // page ids of chunk (i/16 + 1) into the buffer chunk i/16 - 1 used
+        const int chunk = (i >> 4) + 1;
+        const int off = 64 * chunk + lane;
+        if (off < npg) dma_saddr_b32(bt_row + p_begin + 64 * chunk, 4 * lane, lds0 + L::IDS_OFF + (chunk & 1) * 256);
       }
       if (i >= 1) {
         const int j = i - 1;
@@ -839,8 +874,12 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
             }
         }
       }
-      // V of tile i must have landed before the barrier
-      if (i < T) wait_vmcnt_n<NDMA>(min(T - 1, i + RV - 2) - i);
+      // K of tile i + 1 and V of tile i must have landed before the barrier:
+      // wait until only the groups issued after both are in flight
+      if (i < T) {
+        const int need = max(i + 1 < T ? pos_k(i + 1) : 0, pos_v(i));
+        wait_vmcnt_n<NDMA>(ck(i) + cv(i) - need);
+      }
       lds_barrier();
       if (flag_set(i & 1)) {
         // ---- rare path: raise the references (output side) ----
