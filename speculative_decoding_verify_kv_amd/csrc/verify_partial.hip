@@ -463,6 +463,11 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     if (lane == 0) flag_ref(8 + wave) = wbad ? 1 : 0;
   }
   h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
+  // 16-byte unit u of staged row rr sits at unit u ^ (rr & QSW): the fragment
+  // reads below take one unit from each of 16 consecutive rows, which would
+  // otherwise all fall in the same LDS banks (rows are 2 D bytes apart)
+  constexpr int QSW = (D / 8 >= 16) ? 15 : 7;
+  auto q_unit = [&](int rr, int u) __attribute__((always_inline)) { return q_lds + rr * D + 8 * (u ^ (rr & QSW)); };
 #pragma unroll
   for (int u = 0; u < QU_MAX; ++u) {
     const int idx = tid + u * kBlockThreads;
@@ -474,7 +479,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         h16x4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = (h16)x[e];
-        *reinterpret_cast<h16x4*>(q_lds + rr * D + 4 * c) = h;
+        *reinterpret_cast<h16x4*>(q_unit(rr, c >> 1) + 4 * (c & 1)) = h;
       } else if (p.q_dtype == kBF16) {
         h16x8 h;
 #pragma unroll
@@ -482,9 +487,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
           h[2 * e] = (h16)__builtin_bit_cast(float, w[e] << 16);
           h[2 * e + 1] = (h16)__builtin_bit_cast(float, w[e] & 0xffff0000u);
         }
-        *reinterpret_cast<h16x8*>(q_lds + rr * D + 8 * c) = h;
+        *reinterpret_cast<h16x8*>(q_unit(rr, c)) = h;
       } else {
-        *reinterpret_cast<u32x4*>(q_lds + rr * D + 8 * c) = w;
+        *reinterpret_cast<u32x4*>(q_unit(rr, c)) = w;
       }
     }
   }
@@ -573,7 +578,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         int dim0;
         if constexpr (G::Q8) dim0 = 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1);
         else dim0 = 32 * ks + 8 * g4;
-        qf[ks][nt] = *reinterpret_cast<const h16x8*>(q_lds + rr * D + dim0);
+        qf[ks][nt] = *reinterpret_cast<const h16x8*>(q_unit(rr, dim0 >> 3));
       }
       const int r = rowbase + rr;
       brow[nt] = (r < M) ? r % B : 0;
