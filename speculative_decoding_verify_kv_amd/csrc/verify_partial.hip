@@ -208,14 +208,17 @@ struct Lay {
 // ---- numeric helpers ---------------------------------------------------------
 __device__ __forceinline__ h16x2 as_h2(uint32_t u) { return __builtin_bit_cast(h16x2, u); }
 
-// 4 int8 (one dword) -> two fp16 pairs holding the exact integers.
-// (b ^ 0x80) placed under exponent byte 0x64 is 1024 + 128 + b; subtracting
-// 1152 leaves b exactly.
+// 4 int8 (one dword) -> two fp16 pairs holding the exact integers: each
+// byte is sign-extended and converted by a byte-selecting v_cvt_f16_i16 into
+// one half of a packed register (4 instructions per dword).
 __device__ __forceinline__ void i8x4_to_h(uint32_t w, h16x2& lo, h16x2& hi) {
-  const uint32_t x = w ^ 0x80808080u;
-  const h16x2 bias = {(h16)1152.0f, (h16)1152.0f};
-  lo = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
-  hi = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+  uint32_t a, c;
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(a) : "v"(w));
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1" : "+v"(a) : "v"(w));
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(c) : "v"(w));
+  asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3" : "+v"(c) : "v"(w));
+  lo = as_h2(a);
+  hi = as_h2(c);
 }
 
 __device__ __forceinline__ h16x8 cat(h16x2 a, h16x2 b, h16x2 c, h16x2 d) {
