@@ -94,6 +94,26 @@ def test_q8_long(name, S_):
     assert np.abs(lse - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
 
 
+@pytest.mark.parametrize("S_", [1, 0])
+def test_q8_full_byte_range(S_):
+    """Every int8 value dequantises exactly, -128 included (symmetric
+    quantisation never writes it, but a pool may hold it): K and V bytes
+    drawn uniformly from [-128, 127] over the whole pool."""
+    import dataclasses
+
+    base = S.q8_long(ctx=2048)
+    rng = np.random.default_rng(7)
+    w = dataclasses.replace(base, k_pool=rng.integers(-128, 128, base.k_pool.shape, dtype=np.int8),
+                            v_pool=rng.integers(-128, 128, base.v_pool.shape, dtype=np.int8))
+    assert (w.k_pool == -128).any() and (w.v_pool == -128).any() and (w.k_pool == 127).any()
+    say(f"[case] q8 full byte range S={S_}")
+    o, l = oracle.attention(w)
+    got, lse, flags, info = run_gpu(w, S_, "f32")
+    assert flags == 0
+    check_parity(got, o, "f32", f"q8 full byte range S={S_}")
+    assert np.abs(lse - l).max() <= 2e-3
+
+
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_q8_out_dtypes(out_dtype):
     w, o, l = wl("q8_8192")
