@@ -320,3 +320,23 @@ def test_short_splits(ctx, S_):
     ref, _ = oracle.attention(w)
     got = run_gpu(w, S_, "f32")[0]
     check_parity(got, ref, "f32", f"ctx={ctx} S={S_}")
+
+
+@pytest.mark.parametrize("S_", [0, 256])
+def test_max_rows_and_splits(S_):
+    """The largest uniform plan: B = 64 rows (the ancestry bitmask width) over
+    24 query heads, 384 rows per KV head in 4 row groups; with the largest
+    split count, every split is a single page (4,096 tokens, 256 pages)."""
+    if "b64" not in _cache:
+        w = S.make_workload("b64", ctx_lens=[4096], B=64, H=24, KVH=4, D=256, q_dtype="bf16", kv_dtype="q8_0",
+                            seed=3, permute=True)
+        say("[oracle] b64")
+        _cache["b64"] = (w,) + oracle.attention(w)
+    w, o, l = _cache["b64"]
+    say(f"[case] B=64 S={S_}")
+    got, lse, flags, info = run_gpu(w, S_, "f16")
+    assert flags == 0
+    if S_:
+        assert info.num_splits == S_ or S_ == 0
+    check_parity(got, o, "f16", f"B=64 S={S_} ({info.row_groups} row groups)")
+    assert np.abs(lse - l).max() <= 2e-3

@@ -224,3 +224,22 @@ def test_ragged_graph_replay_with_live_rows():
         got = out.float().cpu().double().numpy()
         n = int(c[-1])
         check_parity(got[:n], ref[:n], "f16", f"graph replay {rep} rows={n}")
+
+
+@pytest.mark.parametrize("S_", [1, 0])
+def test_longest_prefill_segment(S_):
+    """A 4,096-row prefill segment (the largest ragged row count) beside a
+    5-row direct chain, 4 query heads over 2 KV heads, D 64."""
+    if "r4096" not in _cache:
+        w = S.make_workload("r4096", ctx_lens=[4200, 300], rows=[4096, 5], H=4, KVH=2, D=64, q_dtype="bf16",
+                            kv_dtype="q8_0", seed=4, permute=True,
+                            parent=np.concatenate([S.chain_parent(4096), S.chain_parent(5)]))
+        say("[oracle] r4096")
+        _cache["r4096"] = (w,) + oracle.attention(w)
+    w, ref, lref = _cache["r4096"]
+    say(f"[case] 4096-row segment S={S_}")
+    got, lse, flags, plan = run_ragged(w, S_, "f32")
+    assert flags == 0
+    n = w.total_rows
+    check_parity(got[:n], ref, "f32", f"4096-row segment S={S_}")
+    assert np.abs(lse[:n] - lref).max() <= 2e-3
