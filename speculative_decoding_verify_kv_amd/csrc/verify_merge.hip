@@ -11,7 +11,7 @@
 // the row NaN.
 //
 // One workgroup of 4 waves per (row, head).  Wave w owns splits w, w + 4,
-// ...; it issues the loads of up to 16 of its split rows at once (16 bytes
+// ...; it issues the loads of up to 8 of its split rows at once (16 bytes
 // per lane each at D = 256) before it reads the split headers, so the
 // partial rows are in flight while the weights are formed.  Every lane loads
 // the headers of splits lane, lane + 64, ... and the weight of split k is
@@ -48,7 +48,7 @@ template <int E> struct VecT { typedef float type __attribute__((ext_vector_type
 template <> struct VecT<1> { typedef float type; };
 
 constexpr int kMergeWaves = 4;
-constexpr int kMergeBatch = 16;  // split rows in flight per wave
+constexpr int kMergeBatch = 8;   // split rows in flight per wave
 
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const MergeParams p) {
