@@ -194,7 +194,7 @@ struct Lay {
   static constexpr int IDS_OFF = P_OFF + 2 * P_BUF;  // int32 [2][64] page ids
   static constexpr int ANC_OFF = IDS_OFF + 512;      // uint64 [64] ancestry masks
   static constexpr int EX_OFF = ANC_OFF + 512;       // float [2][16 NT] row exchange
-  static constexpr int FLAG_OFF = EX_OFF + EX_BYTES; // int flags [16]: [0..2] shared, [8..15] one per wave
+  static constexpr int FLAG_OFF = EX_OFF + EX_BYTES; // int flags [16]: [0..3] shared, [8..15] one per wave
   static constexpr int BYTES = FLAG_OFF + 64;
   // Q staging (fp16 [16 NT][D]) during the prologue: the V ring receives
   // nothing before the first iteration.
@@ -340,10 +340,61 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   if (tid < 128 && pb_spec + tid < pe_spec) id_spec = bt_row[pb_spec + tid];
 
   const bool qf32 = p.q_dtype == kF32;
+  h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
+  // 16-byte unit u of staged row rr sits at unit u ^ (rr & QSW): the fragment
+  // reads below take one unit from each of 16 consecutive rows, which would
+  // otherwise all fall in the same LDS banks (rows are 2 D bytes apart)
+  constexpr int QSW = (D / 8 >= 16) ? 15 : 7;
+  auto q_unit = [&](int rr, int u) __attribute__((always_inline)) { return q_lds + rr * D + 8 * (u ^ (rr & QSW)); };
+
+  // 16-bit Q: the output waves copy the group's Q rows into the staging area
+  // with LDS-DMA (slot s of the swizzled layout = its own 16-byte source
+  // unit), so they hold no vector load of their own and can send the first
+  // K tiles right away; the page ids of those tiles (split page 4j + q) come
+  // through the scalar cache.  fp32 Q is loaded below by all threads.
+  int kid[L::RK - 1];
+#pragma unroll
+  for (int j = 0; j < L::RK - 1; ++j) {
+    const int off = pb_spec + 4 * j + (wave - kRoleWaves);
+    kid[j] = 0;
+    if (!is_score && off < pe_spec)
+      kid[j] = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(bt_row + off));
+  }
+  constexpr int QUPR = D / 8;                          // 16-byte units of a 16-bit Q row
+  constexpr int QSPW = QROWS * QUPR / kRoleWaves;      // staging units per output wave
+  constexpr int QDMA = QSPW / 64;                      // LDS-DMA instructions per output wave
+  static_assert(QSPW % 64 == 0, "whole Q DMA instructions");
+  if (!is_score && !qf32) {
+    const int q4 = wave - kRoleWaves;
+    constexpr int RPI = 64 / QUPR;  // staged rows per instruction
+    int rr = (q4 * QSPW + lane) / QUPR;
+    const int phys = lane & (QUPR - 1);
+    const int r_first = min(rowbase + rr, M - 1);
+    int hl = r_first / B;
+    int b = r_first - hl * B;
+    const int dh = RPI / B, db = RPI - dh * B;
+    const int64_t rowb = (int64_t)D * 2;
+    const char* qb = reinterpret_cast<const char*>(p.q);
+    const int64_t off0 = ((r0 + b) * p.H + kvh * p.G + hl) * rowb;  // a valid row for clamped slots
+#pragma unroll
+    for (int k = 0; k < QDMA; ++k) {
+      const bool valid = rowbase + rr < M;  // rows past the group's last are copies of a valid one
+      const int64_t off = valid ? ((r0 + b) * p.H + kvh * p.G + hl) * rowb : off0;
+      dma_vaddr(qb + off + 16 * (phys ^ (rr & QSW)), lds0 + L::QST_OFF + (q4 * QSPW + 64 * k) * 16);
+      rr += RPI;
+      b += db;
+      hl += dh;
+      if (b >= B) {
+        b -= B;
+        ++hl;
+      }
+    }
+  }
+
   const int upr = qf32 ? D / 4 : D / 8;  // 16-byte Q units per row (a power of two)
   constexpr int QU_MAX = (QROWS * (D / 4) + kBlockThreads - 1) / kBlockThreads;
   u32x4 qraw[QU_MAX];
-  {
+  if (qf32) {
     // unit u of this thread is 16-byte column c of group row rr + u * step;
     // row r = hl * B + b is stepped without a division per unit
     const int step = kBlockThreads / upr;
@@ -370,14 +421,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     }
   }
   int par = 0;
-  if (p.parent && lane < B) par = p.parent[r0 + lane];
+  if (p.parent && is_score && lane < B) par = p.parent[r0 + lane];
   // The ancestry bitmask covers 64 rows: a longer sequence (a ragged prefill
   // segment) is a positioned causal chain, and a supplied parent array must
   // say so (parent[i] == i - 1 for every row).
   const bool long_rows = B > 64;
   bool chain_bad = false;
-  if (long_rows && p.parent)
-    for (int i = tid; i < B; i += kBlockThreads) chain_bad |= p.parent[r0 + i] != i - 1;
+  if (long_rows && p.parent && is_score)
+    for (int i = tid; i < B; i += 64 * kRoleWaves) chain_bad |= p.parent[r0 + i] != i - 1;
 
   // ---- validate sequence metadata (device-resident) ----
   bool poison = false;
@@ -386,9 +437,13 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     ctx = 0;
   }
   uint32_t flagbits = poison ? VA_FLAG_BAD_CTX : 0u;
+  // (the score waves check the parent array; wave 0 publishes the result in
+  // flag 3 for the output waves, which read it after the first barrier)
+  bool parent_bad = false;
   if (p.parent) {
-    const bool bad = lane < B && (par < -1 || par >= lane);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0) {
+    const bool bad = is_score && lane < B && (par < -1 || par >= lane);
+    parent_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (parent_bad) {
       poison = true;
       flagbits |= VA_FLAG_BAD_PARENT;
     }
@@ -430,6 +485,62 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     return __builtin_amdgcn_readfirstlane(flag_ref(idx)) != 0;
   };
 
+  // ---- DMA issue ----
+  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * G::KPAGE;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * G::VPAGE;
+  const char* ksbase = reinterpret_cast<const char*>(p.k_scale) + (int64_t)kvh * G::SPB;
+  const char* vsbase = reinterpret_cast<const char*>(p.v_scale) + (int64_t)kvh * G::SPB;
+  const int64_t kstride = (int64_t)p.KVH * G::KPAGE;  // bytes between pages
+  const int64_t vstride = (int64_t)p.KVH * G::VPAGE;
+  const int64_t sstride = (int64_t)p.KVH * G::SPB;
+  bool bad_page = false;
+
+  // Physical id of split page `off` (per lane).  Padding pages past the split
+  // end read page 0 and are masked; an out-of-range id is flagged and replaced.
+  auto page_id = [&](int off) __attribute__((always_inline)) -> int {
+    if (off >= npg) return 0;
+    int id = ids_lds[((off >> 6) & 1) * 64 + (off & 63)];
+    if (id < 0 || id >= p.num_pages) {
+      bad_page = true;
+      id = 0;
+    }
+    return id;
+  };
+
+  // Score wave w: K page w of tile j (1 KB chunks; lane (g, m) of chunk c
+  // carries token m, bytes [64c + 16g, 64c + 16g + 16)), plus its scales.
+  auto issue_k_id = [&](int j, int id) __attribute__((always_inline)) {
+    const uint32_t st = lds0 + L::KR_OFF + (j % RK) * G::K_STAGE;
+    const char* src = kbase + (int64_t)id * kstride;
+    const uint32_t voff = n16 * G::KROW + 16 * g4;
+#pragma unroll
+    for (int c = 0; c < G::KCH; ++c) dma_saddr(src + 64 * c, voff, st + role * G::KPAGE + 1024 * c);
+    if constexpr (G::Q8) {
+      if (lane < D / 16) dma_saddr(ksbase + (int64_t)id * sstride, 16 * lane, st + 4 * G::KPAGE + role * D);
+    }
+  };
+  auto issue_k = [&](int j) __attribute__((always_inline)) {
+    issue_k_id(j, __builtin_amdgcn_readfirstlane(page_id(4 * j + role)));
+  };
+
+  // Output wave q: dims [q*DO, q*DO + DO) of all 4 pages of tile j (lane
+  // (g, m) of chunk (mt, hh) carries page g, dim q*DO + 16mt + m, bytes
+  // [16hh, 16hh + 16) of its 16-token row), plus page q's V scales.
+  auto issue_v = [&](int j) __attribute__((always_inline)) {
+    const int id = page_id(4 * j + g4);
+    const uint32_t st = lds0 + L::VR_OFF + (j % RV) * G::V_STAGE;
+    const char* src = vbase + (int64_t)id * vstride + (int64_t)(role * G::DO + n16) * G::VROW;
+#pragma unroll
+    for (int mt = 0; mt < G::MTO; ++mt)
+#pragma unroll
+      for (int hh = 0; hh < G::VROW / 16; ++hh)
+        dma_vaddr(src + 16 * mt * G::VROW + 16 * hh, st + (role * G::VCH + mt * (G::VROW / 16) + hh) * 1024);
+    if constexpr (G::Q8) {
+      const int idq = __builtin_amdgcn_readlane(id, 16 * role);
+      if (lane < D / 16) dma_saddr(vsbase + (int64_t)idq * sstride, 16 * lane, st + 4 * G::VPAGE + role * D);
+    }
+  };
+
   // ---- prologue stores: page ids of the first 128 pages, ancestry, Q ----
   if (tid < 128) {
     const bool spec_ok = (p_begin == pb_spec) && (npg <= pe_spec - pb_spec);
@@ -460,43 +571,72 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     flag_ref(0) = 0;
     flag_ref(1) = 0;
     flag_ref(2) = 0;
+    flag_ref(3) = parent_bad ? 1 : 0;
   }
   if (long_rows && p.parent) {
     const bool wbad = __builtin_amdgcn_ballot_w64(chain_bad) != 0;
     if (lane == 0) flag_ref(8 + wave) = wbad ? 1 : 0;
   }
-  h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
-  // 16-byte unit u of staged row rr sits at unit u ^ (rr & QSW): the fragment
-  // reads below take one unit from each of 16 consecutive rows, which would
-  // otherwise all fall in the same LDS banks (rows are 2 D bytes apart)
-  constexpr int QSW = (D / 8 >= 16) ? 15 : 7;
-  auto q_unit = [&](int rr, int u) __attribute__((always_inline)) { return q_lds + rr * D + 8 * (u ^ (rr & QSW)); };
+  bool early_k = false;
+  if (qf32) {
 #pragma unroll
-  for (int u = 0; u < QU_MAX; ++u) {
-    const int idx = tid + u * kBlockThreads;
-    const int rr = idx / upr, c = idx % upr;
-    if (rr < QROWS) {
-      const u32x4 w = qraw[u];
-      if (qf32) {
-        const f32x4 x = __builtin_bit_cast(f32x4, w);
+    for (int u = 0; u < QU_MAX; ++u) {
+      const int idx = tid + u * kBlockThreads;
+      const int rr = idx / upr, c = idx % upr;
+      if (rr < QROWS) {
+        const f32x4 x = __builtin_bit_cast(f32x4, qraw[u]);
         h16x4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) h[e] = (h16)x[e];
         *reinterpret_cast<h16x4*>(q_unit(rr, c >> 1) + 4 * (c & 1)) = h;
-      } else if (p.q_dtype == kBF16) {
+      }
+    }
+  } else if (!is_score) {
+    // the first K tiles, when this split starts where it would for
+    // ctx = max_ctx (otherwise after the barrier, from the LDS page ids)
+    early_k = T > 0 && p_begin == pb_spec && npg <= pe_spec - pb_spec;
+    if (early_k) {
+#pragma unroll
+      for (int j = 0; j < RK - 1; ++j) {
+        if (j < T) {
+          const int off = 4 * j + role;
+          int id = kid[j];
+          if (off >= npg) {
+            id = 0;
+          } else if (id < 0 || id >= p.num_pages) {
+            bad_page = true;
+            id = 0;
+          }
+          issue_k_id(j, id);
+        }
+      }
+      // the Q rows have landed once only those K groups are in flight
+      wait_vmcnt_n<NDMA>(min(T, RK - 1));
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
+  __syncthreads();
+  if (!qf32) {
+    if (p.q_dtype == kBF16) {
+      // bf16 -> fp16 in place, one staged 16-byte unit per thread and step
+      for (int su = tid; su < QROWS * QUPR; su += kBlockThreads) {
+        const u32x4 w = *LDS_PTR(u32x4, lds0 + L::QST_OFF + 16 * su);
         h16x8 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           h[2 * e] = (h16)__builtin_bit_cast(float, w[e] << 16);
           h[2 * e + 1] = (h16)__builtin_bit_cast(float, w[e] & 0xffff0000u);
         }
-        *reinterpret_cast<h16x8*>(q_unit(rr, c)) = h;
-      } else {
-        *reinterpret_cast<u32x4*>(q_unit(rr, c)) = w;
+        *LDS_PTR(h16x8, lds0 + L::QST_OFF + 16 * su) = h;
       }
+      __syncthreads();
     }
   }
-  __syncthreads();
+  if (flag_set(3)) {  // the score waves found a bad parent array
+    poison = true;
+    flagbits |= VA_FLAG_BAD_PARENT;
+  }
   if (long_rows && p.parent) {
     bool bad = false;
 #pragma unroll
@@ -506,60 +646,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       flagbits |= VA_FLAG_BAD_PARENT;
     }
   }
-
-  // ---- DMA issue ----
-  const char* kbase = reinterpret_cast<const char*>(p.k_pool) + (int64_t)kvh * G::KPAGE;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pool) + (int64_t)kvh * G::VPAGE;
-  const char* ksbase = reinterpret_cast<const char*>(p.k_scale) + (int64_t)kvh * G::SPB;
-  const char* vsbase = reinterpret_cast<const char*>(p.v_scale) + (int64_t)kvh * G::SPB;
-  const int64_t kstride = (int64_t)p.KVH * G::KPAGE;  // bytes between pages
-  const int64_t vstride = (int64_t)p.KVH * G::VPAGE;
-  const int64_t sstride = (int64_t)p.KVH * G::SPB;
-  bool bad_page = false;
-
-  // Physical id of split page `off` (per lane).  Padding pages past the split
-  // end read page 0 and are masked; an out-of-range id is flagged and replaced.
-  auto page_id = [&](int off) __attribute__((always_inline)) -> int {
-    if (off >= npg) return 0;
-    int id = ids_lds[((off >> 6) & 1) * 64 + (off & 63)];
-    if (id < 0 || id >= p.num_pages) {
-      bad_page = true;
-      id = 0;
-    }
-    return id;
-  };
-
-  // Score wave w: K page w of tile j (1 KB chunks; lane (g, m) of chunk c
-  // carries token m, bytes [64c + 16g, 64c + 16g + 16)), plus its scales.
-  auto issue_k = [&](int j) __attribute__((always_inline)) {
-    const int id = __builtin_amdgcn_readfirstlane(page_id(4 * j + role));
-    const uint32_t st = lds0 + L::KR_OFF + (j % RK) * G::K_STAGE;
-    const char* src = kbase + (int64_t)id * kstride;
-    const uint32_t voff = n16 * G::KROW + 16 * g4;
-#pragma unroll
-    for (int c = 0; c < G::KCH; ++c) dma_saddr(src + 64 * c, voff, st + role * G::KPAGE + 1024 * c);
-    if constexpr (G::Q8) {
-      if (lane < D / 16) dma_saddr(ksbase + (int64_t)id * sstride, 16 * lane, st + 4 * G::KPAGE + role * D);
-    }
-  };
-
-  // Output wave q: dims [q*DO, q*DO + DO) of all 4 pages of tile j (lane
-  // (g, m) of chunk (mt, hh) carries page g, dim q*DO + 16mt + m, bytes
-  // [16hh, 16hh + 16) of its 16-token row), plus page q's V scales.
-  auto issue_v = [&](int j) __attribute__((always_inline)) {
-    const int id = page_id(4 * j + g4);
-    const uint32_t st = lds0 + L::VR_OFF + (j % RV) * G::V_STAGE;
-    const char* src = vbase + (int64_t)id * vstride + (int64_t)(role * G::DO + n16) * G::VROW;
-#pragma unroll
-    for (int mt = 0; mt < G::MTO; ++mt)
-#pragma unroll
-      for (int hh = 0; hh < G::VROW / 16; ++hh)
-        dma_vaddr(src + 16 * mt * G::VROW + 16 * hh, st + (role * G::VCH + mt * (G::VROW / 16) + hh) * 1024);
-    if constexpr (G::Q8) {
-      const int idq = __builtin_amdgcn_readlane(id, 16 * role);
-      if (lane < D / 16) dma_saddr(vsbase + (int64_t)idq * sstride, 16 * lane, st + 4 * G::VPAGE + role * D);
-    }
-  };
 
   const float c2 = p.scale_log2;
   constexpr int fbuf = L::P_BUF;  // bytes of one P buffer
@@ -771,9 +857,11 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     // Output wave q issues every DMA of the loop: page q of each tile's K
     // (and its scales) besides its quarter of V, so the score waves, which
     // bound the loop, issue none.  The K ring is free from the start.
+    if (!early_k) {
 #pragma unroll
-    for (int j = 0; j < RK - 1; ++j)
-      if (j < T) issue_k(j);
+      for (int j = 0; j < RK - 1; ++j)
+        if (j < T) issue_k(j);
+    }
     // tile 0's K must have landed before the score waves' first iteration
     if (T > 0) wait_vmcnt_n<NDMA>(min(T, RK - 1) - 1);
     __syncthreads();  // matches the score waves' Q-fragment barrier
