@@ -199,9 +199,12 @@ struct Lay {
   // Q staging (fp16 [16 NT][D]) during the prologue: the V ring receives
   // nothing before the first iteration.
   static constexpr int QST_BYTES = 16 * NT * D * 2;
-  static constexpr int QST_OFF = VR_OFF;
+  // when the V ring's stages 1.. hold it, stage 0 takes V of tile 0 before
+  // the staging is read (EV)
+  static constexpr bool EV = RV >= 2 && (RV - 1) * G::V_STAGE >= QST_BYTES;
+  static constexpr int QST_OFF = EV ? VR_OFF + G::V_STAGE : VR_OFF;
   static_assert(BYTES <= BUDGET, "LDS budget");
-  static_assert(QST_BYTES <= RV * G::V_STAGE, "Q staging fits the V ring");
+  static_assert(QST_OFF + QST_BYTES <= VR_OFF + RV * G::V_STAGE, "Q staging fits the V ring");
   static_assert(RK >= 2 && RV >= 2, "ring depth");
 };
 
@@ -862,20 +865,24 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       for (int j = 0; j < RK - 1; ++j)
         if (j < T) issue_k(j);
     }
+    constexpr int EV0 = L::EV ? 1 : 0;  // V of tile 0 goes out here too
+    if (EV0 && T > 0) issue_v(0);
     // tile 0's K must have landed before the score waves' first iteration
-    if (T > 0) wait_vmcnt_n<NDMA>(min(T, RK - 1) - 1);
+    if (T > 0) wait_vmcnt_n<NDMA>(min(T, RK - 1) - 1 + EV0);
     __syncthreads();  // matches the score waves' Q-fragment barrier
 
     // DMA groups (one tile's K page or V quarter, NDMA instructions each) in
-    // issue order: K 0 .. RK-2 before the loop; at iteration t, K t+RK-1,
-    // then V 0 .. RV-2 (t = 0) or V t+RV-2 (t > 0), each while below T.
-    // ck(t) / cv(t): K / V groups issued through iteration t.
+    // issue order: K 0 .. RK-2 (and, with EV, V 0) before the loop; at
+    // iteration t, K t+RK-1, then V EV0 .. RV-2 (t = 0) or V t+RV-2 (t > 0),
+    // each while below T.  ck(t) / cv(t): K / V groups issued through
+    // iteration t.
     auto ck = [&](int t) __attribute__((always_inline)) { return min(T, RK + t); };
-    auto cv = [&](int t) __attribute__((always_inline)) { return t < 0 ? 0 : min(T, RV - 1 + t); };
+    auto cv = [&](int t) __attribute__((always_inline)) { return t < 0 ? min(T, EV0) : min(T, RV - 1 + t); };
     // 1-based issue position of K j and of V j
     auto pos_k = [&](int j) __attribute__((always_inline)) { return j <= RK - 2 ? j + 1 : ck(j - RK) + cv(j - RK) + 1; };
     auto pos_v = [&](int j) __attribute__((always_inline)) {
-      if (j <= RV - 2) return ck(0) + j + 1;
+      if (EV0 && j == 0) return ck(-1) + 1;
+      if (j <= RV - 2) return ck(0) + cv(-1) + j + 1 - EV0;
       const int t = j - RV + 2;
       return ck(t) + cv(t - 1) + 1;
     };
@@ -892,9 +899,9 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     for (int i = 0; i <= T; ++i) {
       if (i + RK - 1 < T) issue_k(i + RK - 1);
       if (i == 0) {
-        // the V ring held the Q staging until the barrier above
+        // the V ring's later stages held the Q staging until the barrier above
 #pragma unroll
-        for (int j = 0; j < RV - 1; ++j)
+        for (int j = EV0; j < RV - 1; ++j)
           if (j < T) issue_v(j);
       } else if (i + RV - 2 < T) {
         issue_v(i + RV - 2);
