@@ -12,10 +12,12 @@
 //
 // One workgroup of 4 waves per (row, head).  Wave w owns splits w, w + 4,
 // ...; it issues the loads of up to 8 of its split rows at once (16 bytes
-// per lane each at D = 256) before it reads the split headers, so the
-// partial rows are in flight while the weights are formed.  Every lane loads
-// the headers of splits lane, lane + 64, ... and the weight of split k is
-// taken from its owner lane with a shuffle.  The 4 waves' sums meet in LDS.
+// per lane each at D = 256) first, so the partial rows are in flight while
+// the weights are formed.  Wave 0 alone
+// loads the split headers (lane: splits lane, lane + 64, ...; each is a lone
+// 4-byte read from its own cache line, so one wave's worth is cheaper than
+// four) and hands the weights to the other waves through LDS.  The 4 waves'
+// sums meet in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -71,32 +73,38 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
 #pragma unroll
   for (int b = 0; b < kMergeBatch; ++b) v[b] = load(wave + kMergeWaves * b);
 
-  // split headers: lane holds splits lane + 64 j
-  float mh[HJ], lh[HJ];
-  float M = -INFINITY;
+  // Split headers, read by wave 0 alone (lane: splits lane + 64 j); the
+  // weights reach the other waves through LDS.  M, L and the NaN state stay
+  // in wave 0, which writes the row.
+  __shared__ float wsh[kMaxSplits];
+  float M = -INFINITY, L = 0.f;
   bool nan_row = false;
+  if (wave == 0) {
+    float mh[HJ], lh[HJ];
 #pragma unroll
-  for (int j = 0; j < HJ; ++j) {
-    const int k = lane + 64 * j;
-    mh[j] = -INFINITY;
-    lh[j] = 0.f;
-    if (k < S) {
-      mh[j] = p.part_m[(int64_t)k * p.nrows + R];
-      lh[j] = p.part_l[(int64_t)k * p.nrows + R];
+    for (int j = 0; j < HJ; ++j) {
+      const int k = lane + 64 * j;
+      mh[j] = -INFINITY;
+      lh[j] = 0.f;
+      if (k < S) {
+        mh[j] = p.part_m[(int64_t)k * p.nrows + R];
+        lh[j] = p.part_l[(int64_t)k * p.nrows + R];
+      }
+      nan_row |= (lh[j] != lh[j]);
+      if (lh[j] > 0.f) M = fmaxf(M, mh[j]);
     }
-    nan_row |= (lh[j] != lh[j]);
-    if (lh[j] > 0.f) M = fmaxf(M, mh[j]);
-  }
-  M = wave_max(M);
-  nan_row = __builtin_amdgcn_ballot_w64(nan_row) != 0;
-  float wh[HJ];
-  float Lpart = 0.f;
+    M = wave_max(M);
+    nan_row = __builtin_amdgcn_ballot_w64(nan_row) != 0;
+    float Lpart = 0.f;
 #pragma unroll
-  for (int j = 0; j < HJ; ++j) {
-    wh[j] = (lh[j] > 0.f) ? __builtin_amdgcn_exp2f(mh[j] - M) : 0.f;
-    Lpart += wh[j] * lh[j];
+    for (int j = 0; j < HJ; ++j) {
+      const float wk = (lh[j] > 0.f) ? __builtin_amdgcn_exp2f(mh[j] - M) : 0.f;
+      Lpart += wk * lh[j];
+      wsh[lane + 64 * j] = wk;
+    }
+    L = wave_sum(Lpart);
   }
-  const float L = wave_sum(Lpart);
+  __syncthreads();
 
   float acc[E];
 #pragma unroll
@@ -109,11 +117,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
       const int k = k0 + kMergeWaves * b;  // wave-uniform
-      float w = 0.f;
-#pragma unroll
-      for (int j = 0; j < HJ; ++j)
-        if ((k >> 6) == j) w = __shfl(wh[j], k & 63);
-      if (k >= S) w = 0.f;
+      const float w = (k < S) ? wsh[min(k, S - 1)] : 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float x;
