@@ -322,11 +322,13 @@ def test_short_splits(ctx, S_):
     check_parity(got, ref, "f32", f"ctx={ctx} S={S_}")
 
 
-@pytest.mark.parametrize("S_", [0, 256])
+@pytest.mark.parametrize("S_", [0, 65, 129, 200, 256])
 def test_max_rows_and_splits(S_):
     """The largest uniform plan: B = 64 rows (the ancestry bitmask width) over
     24 query heads, 384 rows per KV head in 4 row groups; with the largest
-    split count, every split is a single page (4,096 tokens, 256 pages)."""
+    split count, every split is a single page (4,096 tokens, 256 pages).
+    S = 65, 129 and 200 leave empty trailing splits (weight 0 in the merge)
+    and put split headers past the first 64 of a row."""
     if "b64" not in _cache:
         w = S.make_workload("b64", ctx_lens=[4096], B=64, H=24, KVH=4, D=256, q_dtype="bf16", kv_dtype="q8_0",
                             seed=3, permute=True)
