@@ -10,14 +10,13 @@
 // 0 and their O is never used; a NaN l (a split that saw bad metadata) makes
 // the row NaN.
 //
-// One workgroup of 4 waves per (row, head).  Wave w owns splits w, w + 4,
-// ...; it issues the loads of up to 8 of its split rows at once (16 bytes
+// One workgroup of 8 waves per (row, head).  Wave w owns splits w, w + 8,
+// ...; it issues the loads of up to 4 of its split rows at once (16 bytes
 // per lane each at D = 256) first, so the partial rows are in flight while
-// the weights are formed.  Wave 0 alone
-// loads the split headers (lane: splits lane, lane + 64, ...; each is a lone
-// 4-byte read from its own cache line, so one wave's worth is cheaper than
-// four) and hands the weights to the other waves through LDS.  The 4 waves'
-// sums meet in LDS.
+// the weights are formed.  Wave 0 alone loads the split headers (lane:
+// splits lane, lane + 64, ...; each is a lone 4-byte read from its own cache
+// line, so one wave's worth is cheaper than eight) and hands the weights to
+// the other waves through LDS.  The 8 waves' sums meet in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,8 +48,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int E> struct VecT { typedef float type __attribute__((ext_vector_type(E))); };
 template <> struct VecT<1> { typedef float type; };
 
-constexpr int kMergeWaves = 4;
-constexpr int kMergeBatch = 8;   // split rows in flight per wave
+constexpr int kMergeWaves = 8;
+constexpr int kMergeBatch = 4;   // split rows in flight per wave
 
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const MergeParams p) {
