@@ -12,11 +12,12 @@
 //
 // One workgroup of 8 waves per (row, head).  Wave w owns splits w, w + 8,
 // ...; it issues the loads of up to 4 of its split rows at once (16 bytes
-// per lane each at D = 256) first, so the partial rows are in flight while
-// the weights are formed.  Wave 0 alone loads the split headers (lane:
-// splits lane, lane + 64, ...; each is a lone 4-byte read from its own cache
-// line, so one wave's worth is cheaper than eight) and hands the weights to
-// the other waves through LDS.  The 8 waves' sums meet in LDS.
+// per lane each at D = 256) right away, so the partial rows are in flight
+// while the weights are formed.  Wave 0 alone loads the split headers, just
+// before its rows (lane: splits lane, lane + 64, ...; each is a lone 4-byte
+// read from its own cache line, so one wave's worth is cheaper than eight),
+// and hands the weights to the other waves through LDS.  The 8 waves' sums
+// meet in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -68,18 +69,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   auto load = [&](int k) __attribute__((always_inline)) -> vec {
     return *reinterpret_cast<const vec*>(base + (int64_t)min(k, S - 1) * kstride);  // clamped: weight 0 below
   };
-  vec v[kMergeBatch];
-#pragma unroll
-  for (int b = 0; b < kMergeBatch; ++b) v[b] = load(wave + kMergeWaves * b);
-
-  // Split headers, read by wave 0 alone (lane: splits lane + 64 j); the
-  // weights reach the other waves through LDS.  M, L and the NaN state stay
-  // in wave 0, which writes the row.
-  __shared__ float wsh[kMaxSplits];
-  float M = -INFINITY, L = 0.f;
-  bool nan_row = false;
+  // Split headers, read by wave 0 alone (lane: splits lane + 64 j) ahead of
+  // its partial rows, so the weights are ready first; they reach the other
+  // waves through LDS.  M, L and the NaN state stay in wave 0, which writes
+  // the row.
+  float mh[HJ], lh[HJ];
   if (wave == 0) {
-    float mh[HJ], lh[HJ];
 #pragma unroll
     for (int j = 0; j < HJ; ++j) {
       const int k = lane + 64 * j;
@@ -89,6 +84,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
         mh[j] = p.part_m[(int64_t)k * p.nrows + R];
         lh[j] = p.part_l[(int64_t)k * p.nrows + R];
       }
+    }
+  }
+  vec v[kMergeBatch];
+#pragma unroll
+  for (int b = 0; b < kMergeBatch; ++b) v[b] = load(wave + kMergeWaves * b);
+
+  __shared__ float wsh[kMaxSplits];
+  float M = -INFINITY, L = 0.f;
+  bool nan_row = false;
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < HJ; ++j) {
       nan_row |= (lh[j] != lh[j]);
       if (lh[j] > 0.f) M = fmaxf(M, mh[j]);
     }
