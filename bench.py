@@ -7,6 +7,11 @@ bf16 Q, fp16 output, synthetic seeded data.  A step is one verify_attn_run
 already resident in HBM.  Eight distinct KV pools (8 x 71 MB, well beyond the
 256 MB Infinity Cache) are rotated so every step streams cold KV.
 
+With --configs it instead times the other workload shapes (fp16 KV at 8K,
+8-bit KV at 8K / 20,676 / 32,768, the paged four-sequence batch, the draft
+tree and the chain sweep B = 4, 8, 16, 32), one JSON line each, with the
+same cold-pool rotation; the default run prints only the headline line.
+
 Prints one JSON line.  value = KV bytes of the valid tokens / time per call
 (GB/s); roofline = the partial kernel's algorithmic KV bytes / its average
 duration (HIP events around back-to-back launches on the launch stream)
@@ -66,7 +71,73 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="0 = the plan's heuristic")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--pools", type=int, default=NPOOLS)
+    ap.add_argument("--configs", action="store_true", help="time the other workload shapes instead")
     return ap.parse_args()
+
+
+# (label, workload factory, split counts timed; 0 = the plan's heuristic)
+def config_list(S):
+    return [
+        ("fp16 KV, D 256, ctx 8192", lambda: S.qwen_dense(ctx=8192, D=256), (0, 8)),
+        ("fp16 KV, D 128, ctx 8192", lambda: S.qwen_dense(ctx=8192, D=128), (0, 8)),
+        ("8-bit KV, ctx 8192", lambda: S.q8_long(ctx=8192), (0, 8)),
+        ("8-bit KV, ctx 20676", lambda: S.q8_long(ctx=20676), (0, 8)),
+        ("8-bit KV, ctx 32768", lambda: S.q8_long(ctx=32768), (0, 8)),
+        ("paged 4 x B 16, ctx 1016/1024/1032/40000", lambda: S.paged_ragged(), (0, 8)),
+        ("tree 2 direct + 8 tree rows, ctx 20676", lambda: S.tree_mixed(), (0,)),
+        ("chain B 4, ctx 20676", lambda: S.chain(4), (0,)),
+        ("chain B 8, ctx 20676", lambda: S.chain(8), (0,)),
+        ("chain B 16, ctx 20676", lambda: S.chain(16), (0,)),
+        ("chain B 32, ctx 20676", lambda: S.chain(32), (0,)),
+    ]
+
+
+def time_configs(args, torch, va, vdev, S):
+    """One JSON line per (workload, split count): whole-call time over cold,
+    rotated KV pools (at least 8 and at least ~600 MB of KV in rotation)."""
+    stream = torch.cuda.current_stream()
+    for label, make, splits in config_list(S):
+        w = make()
+        dev = vdev.to_device(w)
+        names = [n for n in ("k_pool", "v_pool", "k_scale", "v_scale") if dev[n] is not None]
+        pool_bytes = sum(dev[n].numel() * dev[n].element_size() for n in names)
+        npools = min(64, max(args.pools, -(-600_000_000 // pool_bytes)))
+        pools = [{n: dev[n] for n in names}]
+        for r in range(1, npools):
+            pools.append({n: torch.roll(dev[n], shifts=r * 7, dims=0).contiguous() for n in names})
+        tables = [torch.remainder(dev["block_table"] + r * 7, w.num_pages).to(torch.int32).contiguous()
+                  for r in range(npools)]
+        out, lse = vdev.empty_out(w, w.out_dtype)
+        kv_bytes = w.kv_bytes_valid()
+        for sp in splits:
+            plan = va.verify_attn_plan(vdev.problem_for(w), sp, 0)
+            ws = vdev.workspace(plan)
+
+            def call(i):
+                pl = pools[i % npools]
+                va.verify_attn_run(plan, dev["q"], pl["k_pool"], pl["v_pool"], pl.get("k_scale"), pl.get("v_scale"),
+                                   tables[i % npools], dev["ctx_lens"], dev["parent"], sp, out, lse, ws,
+                                   stream=stream)
+
+            for i in range(args.warmup):
+                call(i)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(args.steps):
+                call(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / args.steps
+            info = plan.info()
+            gbps = kv_bytes / (us * 1e-6) / 1e9
+            print(json.dumps({"config": label, "workload": w.name, "splits": info.num_splits,
+                              "row_groups": info.row_groups, "us_per_call": round(us, 2),
+                              "kv_bytes_per_call": kv_bytes, "GBps": round(gbps, 1),
+                              "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "kv_pools_rotated": npools,
+                              "flags": va.verify_attn_read_flags(plan, ws, stream)}), flush=True)
+        del pools, tables, dev
 
 
 def main():
@@ -89,6 +160,9 @@ def main():
         vbuild.build()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.configs:
+        time_configs(args, torch, va, vdev, S)
+        return
 
     t0 = time.time()
     w = S.q8_long(ctx=args.ctx)

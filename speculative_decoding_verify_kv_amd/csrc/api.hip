@@ -11,6 +11,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include "va_internal.h"
@@ -49,29 +50,19 @@ va_status check_problem(const va_problem* p) {
   return VA_OK;
 }
 
-// Bytes of K plus V (plus scales) one (token, KV head) occupies.
-int64_t kv_bytes_per_token_head(const va_problem& p) {
-  if (p.kv_dtype == VA_Q8_0) return 2 * ((int64_t)p.head_dim + 2 * (p.head_dim / 32));
-  return 2 * 2 * (int64_t)p.head_dim;
-}
-
 // Split-count model.  Work units are (sequence, KV head, row group, split);
-// the partial kernel runs one workgroup per CU.  Size S so that one sequence
-// at max_ctx alone fills every CU, then cap it so that
-//   - every split keeps at least one page pair per wave (8 pages), and
-//   - the fp32 partials written and re-read (S * rows * (D+2) * 4 bytes) stay
-//     below half of the KV bytes streamed, since they cost bandwidth too.
+// the partial kernel runs one workgroup per CU, and a split's time is a fixed
+// part plus one step per 64-token tile.  So: size the splits such that
+// num_seqs sequences at max_ctx fill the CUs once (never a straggler second
+// round), give every split whole tiles, at least two of them, and take the
+// fewest splits with that many tiles, since each split also writes fp32
+// partials that the merge reads back.
 int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
-  const int64_t units = (int64_t)p.num_kv_heads * t.row_groups;
-  int64_t S = ceil_div(cus, units);
+  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * t.row_groups;
+  const int64_t s0 = std::max<int64_t>(1, cus / units);
   const int64_t npages = ceil_div(p.max_ctx, va::kPage);
-  const int64_t s_pages = npages / 8;
-  if (S > s_pages) S = s_pages;
-  const int64_t nrows = rows_capacity(p) * p.num_q_heads;
-  const double part_per_split = (double)nrows * (p.head_dim + 2) * 4.0;
-  const double kv = (double)p.num_seqs * p.max_ctx * p.num_kv_heads * kv_bytes_per_token_head(p);
-  const int64_t s_bytes = (int64_t)(0.5 * kv / part_per_split);
-  if (S > s_bytes) S = s_bytes;
+  const int64_t tiles = std::max<int64_t>(2, ceil_div(npages, 4 * s0));
+  int64_t S = ceil_div(npages, 4 * tiles);
   if (S > va::kMaxSplits) S = va::kMaxSplits;
   if (S < 1) S = 1;
   return (int32_t)S;

@@ -72,11 +72,18 @@ def test_headline_plan_and_workspace(lib):
 def test_heuristic_bounds(lib, cus):
     p = va.verify_attn_plan_for_cus(qwen(), 0, cus)
     info = p.info()
+    units = 4 * info.row_groups
     assert 1 <= info.num_splits <= 256
-    # at least one page pair per wave (8 pages) per split
-    assert info.pages_per_split >= 8
-    # enough splits to fill the CUs when the context allows it
-    assert info.num_splits * 4 * info.row_groups >= min(cus, 4 * info.row_groups * (2048 // 8))
+    # whole 64-token tiles, at least two, per split
+    assert info.pages_per_split >= 8 and info.pages_per_split % 4 == 0
+    tiles = info.pages_per_split // 4
+    # one round of workgroups at most ...
+    assert info.num_splits * units <= max(cus, units)
+    # ... and no fewer tiles per split would still fit in it
+    if tiles > 2 and cus >= units:
+        assert -(-2048 // (4 * (tiles - 1))) * units > cus
+    # the fewest splits with that many tiles
+    assert -(-2048 // info.pages_per_split) == info.num_splits
 
 
 def test_explicit_splits_and_direct(lib):
@@ -98,21 +105,31 @@ def test_row_tiling(lib, B, G, D, nt, rg):
 
 
 def test_small_context_caps_splits(lib):
-    # page cap binds: 16 pages / 8 pages per split
+    # two tiles (8 pages) per split at least: 16 pages give 2 splits
     prob = qwen(rows_per_seq=1, num_q_heads=4, head_dim=64, max_ctx=256, max_pages_per_seq=16, num_pages=16)
     assert va.verify_attn_plan_for_cus(prob, 0, 256).info().num_splits == 2
-    # partial-bytes cap binds: 384 rows of fp32 partials outweigh 256 tokens of KV
     prob = qwen(max_ctx=256, max_pages_per_seq=16, num_pages=16)
-    assert va.verify_attn_plan_for_cus(prob, 0, 256).info().num_splits == 1
+    assert va.verify_attn_plan_for_cus(prob, 0, 256).info().num_splits == 2
+    # 2,048 tokens: 128 pages, 16 splits of 2 tiles
+    prob = qwen(max_ctx=2048, max_pages_per_seq=128, num_pages=128)
+    assert va.verify_attn_plan_for_cus(prob, 0, 256).info().num_splits == 16
+    # 20,676 tokens: 1,293 pages; 64 splits would need 6 tiles each anyway, so 54
+    prob = qwen(max_ctx=20676, max_pages_per_seq=1293, num_pages=1293)
+    info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
+    assert info.num_splits == 54 and info.pages_per_split == 24
 
 
-def test_partial_bytes_cap(lib):
-    # many equal sequences: the fp32 partials must stay below half of the KV bytes
+def test_many_sequences_fill_the_cus_once(lib):
+    # 32 sequences x 4 KV heads = 128 units: 2 splits of 64 tiles each, one
+    # round of 256 workgroups
     prob = qwen(num_seqs=32, max_ctx=8192, max_pages_per_seq=512, num_pages=32 * 512)
     info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
-    nrows = 32 * 16 * 24
-    kv = 32 * 8192 * 4 * 2 * (256 + 16)
-    assert info.num_splits * nrows * 258 * 4 <= 0.5 * kv
+    assert info.num_splits == 2 and info.pages_per_split == 256
+    # 6 KV heads: floor(256 / 6) = 42 splits, never a 43rd that would spill
+    # two workgroups into a second round
+    prob = qwen(num_q_heads=24, num_kv_heads=6)
+    info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
+    assert info.num_splits * 6 * info.row_groups <= 256
 
 
 @pytest.mark.parametrize("kw,status", [
