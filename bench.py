@@ -138,6 +138,131 @@ def time_configs(args, torch, va, vdev, S):
                               "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "kv_pools_rotated": npools,
                               "flags": va.verify_attn_read_flags(plan, ws, stream)}), flush=True)
         del pools, tables, dev
+    time_next_rows(args, torch, va, vdev, S)
+
+
+def _rows_to_device(torch, a):
+    import numpy as np
+
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+
+def time_next_rows(args, torch, va, vdev, S):
+    """Timings of the steps around the attention call: the KV append and
+    8-bit quantisation of the drafted rows, the same attention call replayed
+    from a captured graph, the promotion of an accepted tree path, and a
+    ragged call mixing prefill segments, direct rows and a tree."""
+    import numpy as np
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for i in range(min(n, 200)):
+            fn(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / n
+
+    def emit(label, w, us, extra):
+        print(json.dumps({"config": label, "workload": w.name, "us_per_call": round(us, 2), **extra}), flush=True)
+
+    # KV append + quantise of the 16 drafted rows (bf16 in, 8-bit pool)
+    w = S.q8_long(ctx=32768)
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w), 0, 0)
+    ws = vdev.workspace(plan)
+    k_new, v_new = S.new_kv_rows(w, "bf16", seed=1)
+    kn, vn = _rows_to_device(torch, k_new), _rows_to_device(torch, v_new)
+    us = timed(lambda i: va.verify_attn_append_kv(plan, kn, vn, "bf16", dev["k_pool"], dev["v_pool"], dev["k_scale"],
+                                                  dev["v_scale"], dev["block_table"], dev["ctx_lens"], ws,
+                                                  stream=stream), args.steps)
+    emit("append + quantise 16 rows x 4 KV heads (bf16 -> 8-bit)", w, us,
+         {"flags": va.verify_attn_read_flags(plan, ws, stream)})
+
+    # the headline attention call, 8 calls captured in one graph and replayed
+    out, lse = vdev.empty_out(w, "f16")
+    npools = 8
+    pools = [(dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"])]
+    for r in range(1, npools):
+        pools.append(tuple(torch.roll(t, shifts=r * 7, dims=0).contiguous() for t in pools[0]))
+    tables = [torch.remainder(dev["block_table"] + r * 7, w.num_pages).to(torch.int32).contiguous()
+              for r in range(npools)]
+
+    def call(i, st):
+        k, v, ks, vs = pools[i % npools]
+        va.verify_attn_run(plan, dev["q"], k, v, ks, vs, tables[i % npools], dev["ctx_lens"], None, 0, out, lse, ws,
+                           stream=st)
+
+    eager = timed(lambda i: call(i, stream), args.steps)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            cs = torch.cuda.current_stream()
+            for i in range(npools):
+                call(i, cs)
+    stream.wait_stream(side)
+    replay = timed(lambda i: g.replay(), max(1, args.steps // npools)) / npools
+    kv = w.kv_bytes_valid()
+    emit("headline call replayed from a captured graph (8 calls per graph)", w, replay,
+         {"eager_us_per_call": round(eager, 2), "GBps": round(kv / (replay * 1e-6) / 1e9, 1),
+          "flags": va.verify_attn_read_flags(plan, ws, stream)})
+    del pools, tables, g, dev
+
+    # promotion of an accepted path of a width-8 tree (4 sequences)
+    rng = np.random.default_rng(71)
+    ctxs = (40, 300, 1033, 5000)
+    par = np.stack([S.tree_parent(2, 8, rng) for _ in ctxs])
+    w = S.make_workload("promote", ctx_lens=list(ctxs), B=10, H=24, KVH=4, D=256, q_dtype="bf16", kv_dtype="q8_0",
+                        seed=71, permute=True, spare_pages=5, poison=True, parent=par)
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w), 1, 0)
+    wsb = va.verify_attn_promote_workspace_bytes(plan)
+    pws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    acc = np.zeros((w.num_seqs, w.B), np.int32)
+    n = np.zeros(w.num_seqs, np.int32)
+    for s_ in range(w.num_seqs):
+        node = w.B - 1  # root-first tree path to the last node
+        pth = [node]
+        while par[s_][pth[-1]] >= 2:
+            pth.append(int(par[s_][pth[-1]]))
+        pth = pth[::-1]
+        acc[s_, :len(pth)] = pth
+        n[s_] = len(pth)
+    acc_d = torch.from_numpy(acc).cuda()
+    n_d = torch.from_numpy(n).cuda()
+    new_ctx = torch.zeros(w.num_seqs, dtype=torch.int32, device="cuda")
+    us = timed(lambda i: va.verify_attn_promote_kv(plan, acc_d, n_d, dev["parent"], dev["k_pool"], dev["v_pool"],
+                                                   dev["k_scale"], dev["v_scale"], dev["block_table"],
+                                                   dev["ctx_lens"], new_ctx, pws, wsb, stream=stream), args.steps)
+    emit("promote an accepted tree path (4 sequences, B 10)", w, us,
+         {"accepted_rows": n.tolist(), "flags": va.verify_attn_read_flags(plan, pws, stream)})
+    del dev
+
+    # ragged rows: prefill segments, direct rows and a tree in one call
+    w = S.mixed_lowering()
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w), 0, 0)
+    ws = vdev.workspace(plan)
+    cap = plan.problem.max_total_rows
+    out = torch.empty((cap, w.H, w.D), dtype=torch.float16, device="cuda")
+    lse = torch.empty((cap, w.H), dtype=torch.float32, device="cuda")
+    us = timed(lambda i: va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
+                                                   dev["v_scale"], dev["block_table"], dev["ctx_lens"],
+                                                   dev["cu_rows"], dev["parent"], 0, out, lse, ws, stream=stream),
+               args.steps)
+    kv = w.kv_bytes_valid()
+    emit("ragged: prefill 100 + 37 rows, 2 direct rows, 2 direct + 8 tree rows", w, us,
+         {"splits": plan.info().num_splits, "rows": int(w.cu_rows[-1]), "kv_bytes_per_call": kv,
+          "GBps": round(kv / (us * 1e-6) / 1e9, 1), "flags": va.verify_attn_read_flags(plan, ws, stream)})
 
 
 def main():

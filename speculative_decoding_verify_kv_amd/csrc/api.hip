@@ -56,9 +56,13 @@ va_status check_problem(const va_problem* p) {
 // num_seqs sequences at max_ctx fill the CUs once (never a straggler second
 // round), give every split whole tiles, at least two of them, and take the
 // fewest splits with that many tiles, since each split also writes fp32
-// partials that the merge reads back.
+// partials that the merge reads back.  A ragged plan mixes prefill segments,
+// short decoders and long ones in one call: it is sized for one long decode
+// sequence (one row group) filling the CUs, and its shorter sequences keep
+// to fewer splits by themselves (kMinSplitPages).
 int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
-  const int64_t units = (int64_t)p.num_seqs * p.num_kv_heads * t.row_groups;
+  const int64_t units = ragged(p) ? (int64_t)p.num_kv_heads
+                                  : (int64_t)p.num_seqs * p.num_kv_heads * t.row_groups;
   const int64_t s0 = std::max<int64_t>(1, cus / units);
   const int64_t npages = ceil_div(p.max_ctx, va::kPage);
   const int64_t tiles = std::max<int64_t>(2, ceil_div(npages, 4 * s0));
@@ -71,7 +75,7 @@ int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
 size_t workspace_for(const va_problem& p, int S) {
   const size_t nrows = (size_t)rows_capacity(p) * p.num_q_heads;
   if (S <= 1) return va::kHeaderBytes;
-  return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float);
+  return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float) + nrows * sizeof(int32_t);
 }
 
 va_status make_plan(const va_problem* problem, int32_t num_splits, int32_t cus, va_plan** out_plan,
@@ -160,6 +164,8 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
   pp.part_o = part;
   pp.part_m = part + (int64_t)plan->max_splits * nrows * p.head_dim;
   pp.part_l = pp.part_m + (int64_t)plan->max_splits * nrows;
+  // ragged calls split each sequence by its own context (see kMinSplitPages)
+  pp.part_n = ragged(p) ? reinterpret_cast<int32_t*>(pp.part_l + (int64_t)plan->max_splits * nrows) : nullptr;
   pp.num_seqs = p.num_seqs;
   pp.B = p.rows_per_seq;
   pp.total_rows = (int32_t)rows_capacity(p);
@@ -186,6 +192,7 @@ va::MergeParams merge_params(const va::PartialParams& pp, void* out, float* lse)
   mp.part_o = pp.part_o;
   mp.part_m = pp.part_m;
   mp.part_l = pp.part_l;
+  mp.part_n = pp.part_n;
   mp.out = out;
   mp.lse = lse;
   mp.live_rows = pp.cu_rows ? pp.cu_rows + pp.num_seqs : nullptr;

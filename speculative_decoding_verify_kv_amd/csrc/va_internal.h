@@ -15,6 +15,10 @@ constexpr int kMaxSplits = 256;
 constexpr int kMaxRows = 64;         // B limit of a uniform plan (ancestry bitmask width)
 constexpr int kMaxRowsRagged = 4096; // per-sequence row limit of a ragged plan (chains past 64)
 constexpr size_t kHeaderBytes = 256; // workspace flag header
+// Ragged calls: fewest pages a split of a sequence takes (two 64-token
+// tiles).  A sequence shorter than S such splits uses fewer splits, and the
+// rest of its workgroups exit at once.
+constexpr int kMinSplitPages = 8;
 
 // Kernel-side dtype codes (same values as va_dtype).
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kQ8 = 3 };
@@ -35,6 +39,7 @@ struct PartialParams {
   float* part_o;          // [S][nrows][D]
   float* part_m;          // [S][nrows]  (log2 units)
   float* part_l;          // [S][nrows]
+  int32_t* part_n;        // ragged calls: [nrows] splits that hold keys of the row's sequence (written by split 0); else NULL
   uint32_t* flags;
   int32_t num_seqs, B, H, KVH, G, D;  // B: rows per sequence (ragged: the largest count)
   int32_t total_rows;     // ragged: capacity of the packed rows
@@ -52,6 +57,7 @@ struct MergeParams {
   const float* part_o;
   const float* part_m;
   const float* part_l;
+  const int32_t* part_n;
   void* out;
   float* lse;
   const int32_t* live_rows; // ragged: &cu_rows[num_seqs]; rows from live_rows[0] * heads on are skipped

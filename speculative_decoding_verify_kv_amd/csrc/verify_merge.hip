@@ -6,9 +6,12 @@
 // O = sum w_k O_k / sum w_k l_k and lse = ln2 * (M + log2 sum w_k l_k): the
 // merge step of the split-KV schedule on the page "perf(gfx1100): speed up
 // long-context DFlash verify 13.4% with FA2 split-KV and retain HipGraph/Redline
-// PM4" (Performance, batch-16 kernel screen).  Empty splits (l == 0) get weight
-// 0 and their O is never used; a NaN l (a split that saw bad metadata) makes
-// the row NaN.
+// PM4" (Performance, batch-16 kernel screen).  In a ragged call only the
+// first n splits of a row hold keys (n, written by the partial kernel's split
+// 0, is below S for a sequence too short to fill S splits of the minimum
+// size); empty splits
+// (l == 0) get weight 0 and their O is never used; a NaN l (a split that saw
+// bad metadata) makes the row NaN.
 //
 // One workgroup of 8 waves per (row, head).  Wave w owns splits w, w + 8,
 // ...; it issues the loads of up to 4 of its split rows at once (16 bytes
@@ -63,6 +66,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = p.S;
+  // splits that hold keys of this row's sequence (ragged calls: a short
+  // sequence fills fewer than S); the later ones hold stale data and are
+  // never weighed
+  const int Sr = !p.part_n ? S
+                           : max(1, min(S, *reinterpret_cast<const __attribute__((address_space(4))) int*>(
+                                               (uintptr_t)(p.part_n + R))));
   const float* base = p.part_o + R * D + E * lane;
   const int64_t kstride = p.nrows * D;
 
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
       const int k = lane + 64 * j;
       mh[j] = -INFINITY;
       lh[j] = 0.f;
-      if (k < S) {
+      if (k < Sr) {
         mh[j] = p.part_m[(int64_t)k * p.nrows + R];
         lh[j] = p.part_l[(int64_t)k * p.nrows + R];
       }
@@ -115,7 +124,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int k0 = wave; k0 < S; k0 += kMergeWaves * kMergeBatch) {
+  for (int k0 = wave; k0 < Sr; k0 += kMergeWaves * kMergeBatch) {
     if (k0 != wave) {
 #pragma unroll
       for (int b = 0; b < kMergeBatch; ++b) v[b] = load(k0 + kMergeWaves * b);
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
       const int k = k0 + kMergeWaves * b;  // wave-uniform
-      const float w = (k < S) ? wsh[min(k, S - 1)] : 0.f;
+      const float w = (k < Sr) ? wsh[min(k, Sr - 1)] : 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float x;

@@ -270,7 +270,10 @@ __device__ __forceinline__ u32x4 tail_mask(int first, int end) {
 }
 
 // ---- the kernel -------------------------------------------------------------
-template <int D, int KVT, int NT>
+// SQ: split each sequence by its own context with at least kMinSplitPages
+// pages per split (ragged calls, whose sequences differ widely in length);
+// otherwise every sequence takes S equal splits.
+template <int D, int KVT, int NT, bool SQ>
 __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const PartialParams p) {
   using G = Geo<D, KVT>;
   using L = Lay<D, KVT, NT>;
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // while the kernel runs), so no vector wait sits in front of the loads below.
   int ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s));
   const int npg_max = (p.max_ctx + kPage - 1) / kPage;
-  const int pps_spec = (npg_max + p.S - 1) / p.S;
+  const int pps_spec = SQ ? max((npg_max + p.S - 1) / p.S, kMinSplitPages) : (npg_max + p.S - 1) / p.S;
   const int pb_spec = min(split * pps_spec, npg_max);
   const int pe_spec = min(pb_spec + pps_spec, npg_max);
   int id_spec = 0;
@@ -362,6 +365,19 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     kid[j] = 0;
     if (!is_score && off < pe_spec)
       kid[j] = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(bt_row + off));
+  }
+  if constexpr (SQ) {
+    // Splits of a sequence take at least kMinSplitPages pages each, so a
+    // short sequence fills fewer than S of them.  A workgroup past those has
+    // no keys: it leaves before copying anything (split 0 records the count
+    // for the merge).  ctx is already waited for here, ahead of the Q copies.
+    const bool ctx_bad = ctx < B || ctx > p.max_ctx || ctx > p.max_pages * kPage;
+    const int np = ctx_bad ? 0 : (ctx + kPage - 1) / kPage;
+    const int pp = max((np + p.S - 1) / p.S, kMinSplitPages);
+    if (__builtin_expect(split > 0 && split * pp >= np, 0)) {
+      wait_vmcnt<0>();
+      return;
+    }
   }
   constexpr int QUPR = D / 8;                          // 16-byte units of a 16-bit Q row
   constexpr int QSPW = QROWS * QUPR / kRoleWaves;      // staging units per output wave
@@ -455,6 +471,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   }
   const int base = ctx - B;  // slot of drafted row 0
 
+
   // Last key any row of this group can see: row b sees no slot past base + b.
   const int rend = min(rowbase + QROWS, M);
   int bmax = B - 1;
@@ -466,7 +483,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
 
   // ---- this split's pages (cut at the group's last visible key) and tiles of 4 pages ----
   const int npages = (ctx + kPage - 1) / kPage;
-  const int pps = (npages + p.S - 1) / p.S;
+  const int pps = SQ ? max((npages + p.S - 1) / p.S, kMinSplitPages) : (npages + p.S - 1) / p.S;
+  if constexpr (SQ) {
+    if (split == 0 && !p.direct && tid < QROWS && rowbase + tid < M) {
+      // how many splits hold keys of this sequence, for the merge of each row
+      const int r = rowbase + tid, hl = r / B, b = r - hl * B;
+      p.part_n[(r0 + b) * p.H + kvh * p.G + hl] = max(1, (npages + pps - 1) / pps);
+    }
+  }
   const int p_begin = min(split * pps, npages);
   const int p_end = max(p_begin, min(min(p_begin + pps, npages), vis_pages));
   const int npg = p_end - p_begin;
@@ -1079,7 +1103,10 @@ bool partial_supported(int D, int kv_dtype, int nt) {
 template <int D, int KVT, int NT>
 static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.S * p.row_groups), (unsigned)p.KVH, (unsigned)p.num_seqs);
-  hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT>), grid, dim3(kBlockThreads), 0, stream, p);
+  if (p.part_n)
+    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>), grid, dim3(kBlockThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, false>), grid, dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -64,7 +64,9 @@ def test_headline_plan_and_workspace(lib):
     assert info.num_splits == 64 and info.max_splits == 64
     assert info.pages_per_split == 32
     nrows = 1 * 16 * 24
-    assert info.workspace_bytes == 256 + 64 * nrows * (256 + 2) * 4
+    # flag header, then fp32 O, m and l per split and row, then one int32 per
+    # row: how many splits hold keys of the row's sequence
+    assert info.workspace_bytes == 256 + 64 * nrows * (256 + 2) * 4 + nrows * 4
     assert p.workspace_bytes == info.workspace_bytes
 
 
@@ -280,7 +282,12 @@ def test_ragged_plan_sizes_by_packed_rows(lib):
     plan = va.verify_attn_plan_for_cus(prob, 8, 256)
     info = plan.info()
     assert info.rows_per_group == 96 and info.row_groups == 7  # 600 rows -> 38 tiles -> 7 groups of 6
-    assert info.workspace_bytes == 256 + 8 * 149 * 24 * 258 * 4
+    assert info.workspace_bytes == 256 + 8 * 149 * 24 * 258 * 4 + 149 * 24 * 4
+    # the plan's own split count is sized for one long decode sequence (one
+    # row group per KV head) filling the CUs: 2,500 pages in 63 splits of 10
+    # tiles; the shorter sequences of the call keep to fewer splits themselves
+    info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
+    assert info.num_splits == 63 and info.pages_per_split == 40
     # long prefill segments are allowed only in ragged plans
     assert plan_status(qwen(rows_per_seq=65)) == va.VA_EUNSUPPORTED
     assert plan_status(qwen(rows_per_seq=4096, max_total_rows=4096, max_ctx=32768)) == va.VA_OK
