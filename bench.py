@@ -392,7 +392,7 @@ def main():
                    "kv_pools_rotated": args.pools, "kv_bytes_per_call": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(ROOT),
-                     "kernel": "verify_partial_kernel<256,Q8,6>", "kernel_avg_us": round(partial_avg_us, 3),
+                     "kernel": "verify_partial_kernel<256,Q8,6,false>", "kernel_avg_us": round(partial_avg_us, 3),
                      "merge_avg_us": round(merge_avg_us, 3),
                      "mfma": {"tflops": round(mfma_tflops, 1), "peak_tflops": MFMA_PEAK_TFLOPS,
                               "util": round(mfma_tflops / MFMA_PEAK_TFLOPS, 4)}},

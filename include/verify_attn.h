@@ -61,8 +61,10 @@
  * WORKSPACE
  *   verify_attn_plan reports workspace_bytes.  The first 256 bytes hold a
  *   uint32 flag word (kernels OR error bits into it); the rest holds the fp32
- *   split partials.  Zero the workspace once after allocating it; the flags
- *   stay set until verify_attn_read_flags clears them.
+ *   split partials and, last, one int32 per (row, head): the number of splits
+ *   that hold keys of the row's sequence (ragged calls).  Zero the workspace
+ *   once after allocating it; the flags stay set until verify_attn_read_flags
+ *   clears them.
  *
  * ERRORS (fail closed: nothing is launched on any error)
  *   VA_EUNSUPPORTED  shape or dtype outside what the kernels implement
