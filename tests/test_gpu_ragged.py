@@ -243,3 +243,33 @@ def test_longest_prefill_segment(S_):
     n = w.total_rows
     check_parity(got[:n], ref, "f32", f"4096-row segment S={S_}")
     assert np.abs(lse[:n] - lref).max() <= 2e-3
+
+
+@pytest.mark.parametrize("S_", [64, 256])
+def test_short_sequences_leave_their_extra_splits(S_):
+    """Ragged calls split each sequence by its own context into splits of at
+    least 8 pages: contexts of 17, 130 and 4,000 tokens fill 1, 2 and 32 of
+    the S splits, and the workgroups of the other splits write nothing.  The
+    partial area of the workspace is filled with NaN bytes first, so the
+    merge reading any split that was not written would show."""
+    import torch
+
+    w = S.make_workload("short_splits", ctx_lens=[17, 130, 4000, 64], rows=[5, 12, 16, 0], H=24, KVH=4, D=256,
+                        q_dtype="bf16", kv_dtype="q8_0", seed=67, permute=True, spare_pages=3, poison=True)
+    say(f"[case] short sequences S={S_} ctx={w.ctx_lens.tolist()} rows={np.diff(w.cu_rows).tolist()}")
+    ref, lref = oracle.attention(w)
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f32"), S_, 0)
+    ws = vdev.workspace(plan)
+    ws[256:] = 0xFF  # NaN in every fp32 partial slot (the flag header stays zero)
+    cap = plan.problem.max_total_rows
+    out = torch.full((cap, w.H, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((cap, w.H), float("nan"), dtype=torch.float32, device="cuda")
+    va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                              dev["block_table"], dev["ctx_lens"], dev["cu_rows"], dev["parent"], S_, out, lse, ws)
+    torch.cuda.synchronize()
+    assert va.verify_attn_read_flags(plan, ws) == 0
+    n = w.total_rows
+    got = out.cpu().double().numpy()[:n]
+    check_parity(got, ref, "f32", f"short sequences S={S_}")
+    assert np.abs(lse.cpu().double().numpy()[:n] - lref).max() <= 2e-3
