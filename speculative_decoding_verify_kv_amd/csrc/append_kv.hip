@@ -10,9 +10,7 @@
 // -127, 127) in fp32 with the stored fp16 scale; an all-zero block stores
 // scale 0 and codes 0, a NaN entry stores code 0.
 //
-// One thread per (sequence, row, KV head, K or V, 32-entry block).  The work
-// is tiny (B * KVH * 2 * D elements per sequence), so the kernel favours
-// plain per-thread code over coalescing.
+// One wave per (sequence, row, KV head, K or V); see the kernel.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -24,22 +22,17 @@ namespace {
 
 typedef _Float16 h16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef h16 h16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float load_elem(const void* src, int dtype, int64_t idx) {
-  if (dtype == kF32) return reinterpret_cast<const float*>(src)[idx];
-  const uint16_t b = reinterpret_cast<const uint16_t*>(src)[idx];
-  if (dtype == kF16) return (float)__builtin_bit_cast(h16, b);
-  return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
-
+// One wave per (sequence, row, KV head, K or V): lane l holds head_dim
+// entries 4l .. 4l + 3, so a 32-entry block spans 8 lanes and its maximum is
+// taken across them; the per-entry arithmetic is that of the format above.
 __global__ __launch_bounds__(256) void append_kv_kernel(const AppendParams p) {
-  const int NB = p.D / 32;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2 * NB;
+  const int lane = threadIdx.x & 63;
+  int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2;
   if (idx >= total) return;
-  const int blk = (int)(idx % NB);
-  idx /= NB;
   const int which = (int)(idx % 2);  // 0: K, 1: V
   idx /= 2;
   const int g = (int)(idx % p.KVH);
@@ -49,79 +42,95 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const AppendParams p) {
 
   const int ctx = p.ctx_lens[s];
   if (ctx < p.B || ctx > p.max_ctx || ctx > p.max_pages * kPage) {
-    if (i == 0 && g == 0 && which == 0 && blk == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_CTX);
+    if (i == 0 && g == 0 && which == 0 && lane == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_CTX);
     return;
   }
   const int t = ctx - p.B + i;
   const int id = p.block_table[(int64_t)s * p.max_pages + t / kPage];
   if (id < 0 || id >= p.num_pages) {
-    if (g == 0 && which == 0 && blk == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_PAGE);
+    if (g == 0 && which == 0 && lane == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_PAGE);
     return;
   }
   const int slot = t % kPage;
   const int D = p.D;
+  const int NB = D / 32;
+  const bool act = 4 * lane < D;  // whole 8-lane blocks: D / 4 is a multiple of 8
+  const int d0 = 4 * lane;
   const void* src = which ? p.v_new : p.k_new;
-  const int64_t e0 = ((int64_t)(s * p.B + i) * p.KVH + g) * D + 32 * blk;
-  float x[32];
+  const int64_t e0 = ((int64_t)(s * p.B + i) * p.KVH + g) * D + d0;
+  float x[4] = {0.f, 0.f, 0.f, 0.f};
+  if (act) {
+    if (p.new_dtype == kF32) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(src) + e0);
 #pragma unroll
-  for (int e = 0; e < 32; ++e) x[e] = load_elem(src, p.new_dtype, e0 + e);
+      for (int e = 0; e < 4; ++e) x[e] = v[e];
+    } else {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(src) + e0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        x[e] = p.new_dtype == kF16 ? (float)__builtin_bit_cast(h16, (uint16_t)b) : __builtin_bit_cast(float, b << 16);
+      }
+    }
+  }
 
   const int64_t head = (int64_t)id * p.KVH + g;  // (page, KV head) index
   if (p.kv_dtype == kF16) {
+    if (!act) return;
     h16* pool = reinterpret_cast<h16*>(which ? p.v_pool : p.k_pool) + head * kPage * D;
+    if (which) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int d = 32 * blk + e;
-      if (which) pool[(int64_t)d * kPage + slot] = (h16)x[e];
-      else pool[(int64_t)slot * D + d] = (h16)x[e];
+      for (int e = 0; e < 4; ++e) pool[(int64_t)(d0 + e) * kPage + slot] = (h16)x[e];
+    } else {
+      h16x4 h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (h16)x[e];
+      *reinterpret_cast<h16x4*>(pool + (int64_t)slot * D + d0) = h;
     }
     return;
   }
 
   float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < 4; ++e) {
     const float a = __builtin_fabsf(x[e]);
     amax = a > amax ? a : amax;  // a NaN entry never raises the max
   }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    const float a = __shfl_xor(amax, o);
+    amax = a > amax ? a : amax;
+  }
   const h16 dh = (h16)__fdiv_rn(amax, 127.0f);
   const float d16 = (float)dh;
-  int8_t* pool = reinterpret_cast<int8_t*>(which ? p.v_pool : p.k_pool) + head * kPage * D;
-  int8_t q[32];
+  uint32_t packed = 0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
+  for (int e = 0; e < 4; ++e) {
     float r = d16 != 0.f ? __fdiv_rn(x[e], d16) : 0.f;
     if (r != r) r = 0.f;
     r = roundf(r);
     r = fminf(fmaxf(r, -127.f), 127.f);
-    q[e] = (int8_t)(int)r;
+    packed |= (uint32_t)(uint8_t)(int8_t)(int)r << (8 * e);
   }
+  if (!act) return;
+  int8_t* pool = reinterpret_cast<int8_t*>(which ? p.v_pool : p.k_pool) + head * kPage * D;
+  const int blk = lane >> 3;
   if (which) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) pool[(int64_t)(32 * blk + e) * kPage + slot] = q[e];
-    reinterpret_cast<h16*>(p.v_scale)[(head * NB + blk) * kPage + slot] = dh;
+    for (int e = 0; e < 4; ++e) pool[(int64_t)(d0 + e) * kPage + slot] = (int8_t)(packed >> (8 * e));
+    if ((lane & 7) == 0) reinterpret_cast<h16*>(p.v_scale)[(head * NB + blk) * kPage + slot] = dh;
   } else {
-    u32x4 w0, w1;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      w0[k] = (uint32_t)(uint8_t)q[4 * k] | ((uint32_t)(uint8_t)q[4 * k + 1] << 8) |
-              ((uint32_t)(uint8_t)q[4 * k + 2] << 16) | ((uint32_t)(uint8_t)q[4 * k + 3] << 24);
-      w1[k] = (uint32_t)(uint8_t)q[16 + 4 * k] | ((uint32_t)(uint8_t)q[16 + 4 * k + 1] << 8) |
-              ((uint32_t)(uint8_t)q[16 + 4 * k + 2] << 16) | ((uint32_t)(uint8_t)q[16 + 4 * k + 3] << 24);
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(pool + (int64_t)slot * D + 32 * blk);
-    dst[0] = w0;
-    dst[1] = w1;
-    reinterpret_cast<h16*>(p.k_scale)[(head * kPage + slot) * NB + blk] = dh;
+    *reinterpret_cast<uint32_t*>(pool + (int64_t)slot * D + d0) = packed;
+    if ((lane & 7) == 0) reinterpret_cast<h16*>(p.k_scale)[(head * kPage + slot) * NB + blk] = dh;
   }
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendParams& p, hipStream_t stream) {
-  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2 * (p.D / 32);
+  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2;  // waves, 4 per workgroup
   if (total == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((total + 255) / 256);
+  const unsigned blocks = (unsigned)((total + 3) / 4);
   hipLaunchKernelGGL(append_kv_kernel, dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
