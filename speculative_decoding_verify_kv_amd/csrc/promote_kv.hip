@@ -13,7 +13,8 @@
 // every (sequence, path node) and gather the accepted rows into workspace
 // staging (sources and destinations may overlap), (3) if no check failed,
 // scatter the staging rows to their destination slots and write new_ctx.
-// One thread per (sequence, path slot, KV head, K or V, 32-entry block).
+// One wave per (sequence, path slot, KV head, K or V): lane l moves head_dim
+// entries 4l .. 4l + 3 and lane b < D/32 the scale of block b.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -24,16 +25,13 @@ namespace va {
 namespace {
 
 struct Item {
-  int s, k, g, which, blk;
+  int s, k, g, which;
 };
 
 __device__ __forceinline__ bool decode(const PromoteParams& p, Item& it) {
-  const int NB = p.D / 32;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2 * NB;
+  int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2;
   if (idx >= total) return false;
-  it.blk = (int)(idx % NB);
-  idx /= NB;
   it.which = (int)(idx % 2);
   idx /= 2;
   it.g = (int)(idx % p.KVH);
@@ -61,6 +59,49 @@ __device__ __forceinline__ int parent_of(const PromoteParams& p, int s, int r) {
 
 __device__ __forceinline__ char* staging_row(const PromoteParams& p, const Item& it) {
   return p.staging + ((((int64_t)it.s * p.B + it.k) * p.KVH + it.g) * 2 + it.which) * p.row_bytes;
+}
+
+// Lane l's head_dim entries 4l .. 4l + 3 and lane b's block scale between a
+// pool slot and a staging row (dims contiguous, then the D/32 scales):
+// pool -> row when `gather`, else row -> pool.
+__device__ __forceinline__ void copy_row(const PromoteParams& p, const Item& it, int64_t page, int slot, char* row,
+                                         bool gather) {
+  const int lane = threadIdx.x & 63;
+  const int d0 = 4 * lane;
+  char* pool = reinterpret_cast<char*>(it.which ? p.v_pool : p.k_pool);
+  if (d0 < p.D) {
+    if (!it.which) {  // token-major K: the 4 entries are contiguous
+      char* pe = pool + elem(p, 0, page, it.g, slot, d0) * p.esz;
+      char* re = row + (int64_t)d0 * p.esz;
+      if (p.esz == 1) {
+        if (gather) *reinterpret_cast<uint32_t*>(re) = *reinterpret_cast<const uint32_t*>(pe);
+        else *reinterpret_cast<uint32_t*>(pe) = *reinterpret_cast<const uint32_t*>(re);
+      } else {
+        if (gather) *reinterpret_cast<uint2*>(re) = *reinterpret_cast<const uint2*>(pe);
+        else *reinterpret_cast<uint2*>(pe) = *reinterpret_cast<const uint2*>(re);
+      }
+    } else {  // dim-major V: 16 slots apart
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        char* pe = pool + elem(p, 1, page, it.g, slot, d0 + e) * p.esz;
+        char* re = row + (int64_t)(d0 + e) * p.esz;
+        if (p.esz == 1) {
+          if (gather) *re = *pe;
+          else *pe = *re;
+        } else {
+          if (gather) *reinterpret_cast<uint16_t*>(re) = *reinterpret_cast<const uint16_t*>(pe);
+          else *reinterpret_cast<uint16_t*>(pe) = *reinterpret_cast<const uint16_t*>(re);
+        }
+      }
+    }
+  }
+  if (p.kv_is_q8 && lane < p.D / 32) {
+    uint16_t* sc = reinterpret_cast<uint16_t*>(it.which ? p.v_scale : p.k_scale) +
+                   scale_idx(p, it.which, page, it.g, slot, lane);
+    uint16_t* rs = reinterpret_cast<uint16_t*>(row + (int64_t)p.D * p.esz) + lane;
+    if (gather) *rs = *sc;
+    else *sc = *rs;
+  }
 }
 
 __global__ void promote_clear_kernel(uint32_t* status) { *status = 0u; }
@@ -96,26 +137,13 @@ __global__ __launch_bounds__(256) void promote_gather_kernel(const PromoteParams
         if (ps < 0 || ps >= p.num_pages || pd < 0 || pd >= p.num_pages) {
           bad |= VA_FLAG_BAD_PAGE;
         } else {
-          // gather 32 entries (and the scale) of the source row into staging
-          char* row = staging_row(p, it);
-          const int slot = t_src % kPage;
-          const char* pool = reinterpret_cast<const char*>(it.which ? p.v_pool : p.k_pool);
-#pragma unroll 8
-          for (int e = 0; e < 32; ++e) {
-            const int d = 32 * it.blk + e;
-            const int64_t off = elem(p, it.which, ps, it.g, slot, d) * p.esz;
-            for (int b = 0; b < p.esz; ++b) row[(int64_t)d * p.esz + b] = pool[off + b];
-          }
-          if (p.kv_is_q8) {
-            const uint16_t* sc = reinterpret_cast<const uint16_t*>(it.which ? p.v_scale : p.k_scale);
-            reinterpret_cast<uint16_t*>(row + (int64_t)p.D * p.esz)[it.blk] =
-                sc[scale_idx(p, it.which, ps, it.g, slot, it.blk)];
-          }
+          // gather the source row (and its scales) into staging
+          copy_row(p, it, ps, t_src % kPage, staging_row(p, it), true);
         }
       }
     }
   }
-  if (bad) {
+  if (bad && (threadIdx.x & 63) == 0) {
     atomicOr(p.status, bad);
     atomicOr(p.flags, bad);
   }
@@ -127,7 +155,7 @@ __global__ __launch_bounds__(256) void promote_scatter_kernel(const PromoteParam
   const bool ok = (*p.status == 0u);
   const int ctx = p.ctx_lens[it.s];
   const int n = p.n_accepted[it.s];
-  if (it.k == 0 && it.g == 0 && it.which == 0 && it.blk == 0 && p.new_ctx) {
+  if (it.k == 0 && it.g == 0 && it.which == 0 && (threadIdx.x & 63) == 0 && p.new_ctx) {
     int nc = ctx;
     if (ok && n > 0) nc = ctx - p.B + parent_of(p, it.s, p.accepted[(int64_t)it.s * p.B]) + 1 + n;
     else if (ok) nc = ctx - p.B;
@@ -137,19 +165,7 @@ __global__ __launch_bounds__(256) void promote_scatter_kernel(const PromoteParam
   const int r0 = p.accepted[(int64_t)it.s * p.B];
   const int t_dst = ctx - p.B + parent_of(p, it.s, r0) + 1 + it.k;
   const int pd = p.block_table[(int64_t)it.s * p.max_pages + t_dst / kPage];
-  const int slot = t_dst % kPage;
-  const char* row = staging_row(p, it);
-  char* pool = reinterpret_cast<char*>(it.which ? p.v_pool : p.k_pool);
-#pragma unroll 8
-  for (int e = 0; e < 32; ++e) {
-    const int d = 32 * it.blk + e;
-    const int64_t off = elem(p, it.which, pd, it.g, slot, d) * p.esz;
-    for (int b = 0; b < p.esz; ++b) pool[off + b] = row[(int64_t)d * p.esz + b];
-  }
-  if (p.kv_is_q8) {
-    uint16_t* sc = reinterpret_cast<uint16_t*>(it.which ? p.v_scale : p.k_scale);
-    sc[scale_idx(p, it.which, pd, it.g, slot, it.blk)] = reinterpret_cast<const uint16_t*>(row + (int64_t)p.D * p.esz)[it.blk];
-  }
+  copy_row(p, it, pd, t_dst % kPage, staging_row(p, it), false);
 }
 
 }  // namespace
@@ -161,10 +177,10 @@ size_t promote_row_bytes(int D, int kv_dtype) {
 }
 
 hipError_t launch_promote(const PromoteParams& p, hipStream_t stream) {
-  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2 * (p.D / 32);
+  const int64_t total = (int64_t)p.num_seqs * p.B * p.KVH * 2;  // waves, 4 per workgroup
   hipLaunchKernelGGL(promote_clear_kernel, dim3(1), dim3(1), 0, stream, p.status);
   if (total > 0) {
-    const unsigned blocks = (unsigned)((total + 255) / 256);
+    const unsigned blocks = (unsigned)((total + 3) / 4);
     hipLaunchKernelGGL(promote_gather_kernel, dim3(blocks), dim3(256), 0, stream, p);
     hipLaunchKernelGGL(promote_scatter_kernel, dim3(blocks), dim3(256), 0, stream, p);
   }
