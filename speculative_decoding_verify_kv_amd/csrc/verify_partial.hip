@@ -297,10 +297,17 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // Workgroup -> (split, row group).  When every split has several row
   // groups, the row groups of one split get block ids 8 apart: blocks are
   // dealt round-robin to the 8 XCDs, so they share one L2 and run together.
-  const int s = blockIdx.z;
-  const int kvh = blockIdx.y;
+  // Ragged calls (SQ) take the grid as (sequence and KV head, row group,
+  // split counted down): blocks go out in that order, so the high splits,
+  // which only long sequences fill, start first and the short sequences'
+  // few splits fill in behind.
+  const int s = SQ ? (int)(blockIdx.x % p.num_seqs) : (int)blockIdx.z;
+  const int kvh = SQ ? (int)(blockIdx.x / p.num_seqs) : (int)blockIdx.y;
   int split, rg;
-  if (p.row_groups > 1 && (p.S & 7) == 0) {
+  if (SQ) {
+    rg = blockIdx.y;
+    split = p.S - 1 - (int)blockIdx.z;
+  } else if (p.row_groups > 1 && (p.S & 7) == 0) {
     const int x = blockIdx.x, hi = x >> 3;
     rg = hi % p.row_groups;
     split = (hi / p.row_groups) * 8 + (x & 7);
@@ -325,7 +332,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   const int rowbase = rg * QROWS;
   if (rowbase >= M) {
     // no rows of this sequence in this group (nothing is written)
-    if (bad_rows && tid == 0 && blockIdx.x == 0 && kvh == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_ROWS);
+    if (bad_rows && tid == 0 && (SQ ? split == 0 && rg == 0 : blockIdx.x == 0) && kvh == 0)
+      atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_ROWS);
     return;
   }
 
@@ -1104,7 +1112,9 @@ template <int D, int KVT, int NT>
 static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.S * p.row_groups), (unsigned)p.KVH, (unsigned)p.num_seqs);
   if (p.part_n)
-    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>), grid, dim3(kBlockThreads), 0, stream, p);
+    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>),
+                       dim3((unsigned)(p.KVH * p.num_seqs), (unsigned)p.row_groups, (unsigned)p.S),
+                       dim3(kBlockThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, false>), grid, dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
