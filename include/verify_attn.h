@@ -198,7 +198,10 @@ va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool
  * Every other argument as for verify_attn_run.  A sequence's outputs depend
  * only on its own rows, context and pages and on the plan and num_splits.
  * A bad cu_rows entry sets VA_FLAG_BAD_ROWS; that sequence writes nothing
- * (outputs of rows it would own are unspecified).  The grid is fixed by the
+ * (outputs of rows it would own are unspecified).  Sequences before the first
+ * bad entry are unaffected; where a bad entry makes later sequences' rows
+ * overlap earlier ones, those later sequences may be left unwritten too
+ * (the grid holds row groups for max_total_rows rows).  The grid is fixed by the
  * plan, so the call can be captured in a graph with live cu_rows.
  */
 va_status verify_attn_run_ragged(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,

@@ -297,23 +297,60 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // Workgroup -> (split, row group).  When every split has several row
   // groups, the row groups of one split get block ids 8 apart: blocks are
   // dealt round-robin to the 8 XCDs, so they share one L2 and run together.
-  // Ragged calls (SQ) take the grid as (sequence and KV head, row group,
-  // split counted down): blocks go out in that order, so the high splits,
-  // which only long sequences fill, start first and the short sequences'
-  // few splits fill in behind.
-  const int s = SQ ? (int)(blockIdx.x % p.num_seqs) : (int)blockIdx.z;
-  const int kvh = SQ ? (int)(blockIdx.x / p.num_seqs) : (int)blockIdx.y;
-  int split, rg;
-  if (SQ) {
-    rg = blockIdx.y;
+  // Ragged calls (SQ) take the grid as (row group, KV head, split counted
+  // down).  The row groups of all sequences are numbered in sequence order
+  // (sequence s has ceil(rows_s * G / QROWS) of them), so no workgroup is
+  // spent on a group a sequence does not have; each wave finds its sequence
+  // with a prefix sum of those counts over cu_rows, 64 sequences at a time.
+  // Blocks go out in grid order, so the high splits, which only long
+  // sequences fill, start first and the short sequences' few splits fill in
+  // behind.
+  int s, kvh, split, rg;
+  if constexpr (SQ) {
+    kvh = blockIdx.y;
     split = p.S - 1 - (int)blockIdx.z;
-  } else if (p.row_groups > 1 && (p.S & 7) == 0) {
-    const int x = blockIdx.x, hi = x >> 3;
-    rg = hi % p.row_groups;
-    split = (hi / p.row_groups) * 8 + (x & 7);
+    const int g = blockIdx.x;
+    s = -1;
+    rg = 0;
+    int before = 0;
+    bool any_bad = false;
+    for (int base = 0; base < p.num_seqs; base += 64) {
+      const int si = base + lane;
+      int cnt = 0;
+      bool bad = false;
+      if (si < p.num_seqs) {
+        const int a = p.cu_rows[si], e = p.cu_rows[si + 1];
+        bad = a < 0 || e < a || e > p.total_rows || e - a > p.B;
+        cnt = bad ? 0 : ((e - a) * p.G + QROWS - 1) / QROWS;
+      }
+      any_bad |= __ballot(bad) != 0;
+      int inc = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o);
+        if (lane >= o) inc += t;
+      }
+      const uint64_t hit = __ballot(before + inc > g);
+      if (hit && s < 0) {
+        const int l = __builtin_ctzll(hit);
+        s = base + l;
+        rg = g - before - (__builtin_amdgcn_readlane(inc, l) - __builtin_amdgcn_readlane(cnt, l));
+      }
+      before += __builtin_amdgcn_readlane(inc, 63);
+    }
+    if (any_bad && tid == 0 && g == 0 && kvh == 0 && split == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_ROWS);
+    if (s < 0) return;  // past the last sequence's groups
   } else {
-    split = blockIdx.x % p.S;
-    rg = blockIdx.x / p.S;
+    s = blockIdx.z;
+    kvh = blockIdx.y;
+    if (p.row_groups > 1 && (p.S & 7) == 0) {
+      const int x = blockIdx.x, hi = x >> 3;
+      rg = hi % p.row_groups;
+      split = (hi / p.row_groups) * 8 + (x & 7);
+    } else {
+      split = blockIdx.x % p.S;
+      rg = blockIdx.x / p.S;
+    }
   }
   // Rows of this sequence: B each, or (ragged) cu_rows[s] .. cu_rows[s+1]
   // of the packed q / out rows.  Row r of the group list is (head hl, row b)
@@ -1111,10 +1148,17 @@ bool partial_supported(int D, int kv_dtype, int nt) {
 template <int D, int KVT, int NT>
 static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.S * p.row_groups), (unsigned)p.KVH, (unsigned)p.num_seqs);
-  if (p.part_n)
+  if (p.part_n) {
+    // Row groups over all sequences: sum_s ceil(rows_s * G / QROWS) with
+    // sum_s rows_s <= total_rows while cu_rows is valid up to s.
+    constexpr int64_t QR = 16 * NT;
+    const int64_t all = (int64_t)p.num_seqs * p.row_groups;
+    const int64_t bound = ((int64_t)p.total_rows * p.G + (int64_t)p.num_seqs * (QR - 1)) / QR;
+    const int64_t groups = bound < all ? (bound > 1 ? bound : 1) : all;
     hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>),
-                       dim3((unsigned)(p.KVH * p.num_seqs), (unsigned)p.row_groups, (unsigned)p.S),
+                       dim3((unsigned)groups, (unsigned)p.KVH, (unsigned)p.S),
                        dim3(kBlockThreads), 0, stream, p);
+  }
   else
     hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, false>), grid, dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
