@@ -273,3 +273,22 @@ def test_short_sequences_leave_their_extra_splits(S_):
     got = out.cpu().double().numpy()[:n]
     check_parity(got, ref, "f32", f"short sequences S={S_}")
     assert np.abs(lse.cpu().double().numpy()[:n] - lref).max() <= 2e-3
+
+
+@pytest.mark.parametrize("kv,S_", [("q8_0", 0), ("f16", 3)])
+def test_many_sequences(kv, S_):
+    # 150 sequences of 0-4 rows: the kernel numbers row groups over all
+    # sequences with a prefix sum taken 64 sequences at a time, so this spans
+    # three such passes, with empty sequences at and around their edges
+    rng = np.random.default_rng(29)
+    rows = rng.integers(0, 5, 150)
+    rows[[0, 63, 64, 127, 128, 149]] = [0, 0, 3, 0, 2, 0]
+    ctxs = rows + rng.integers(1, 150, 150)
+    w = tiny_ragged(kv, seed=29, rows=tuple(int(r) for r in rows), ctxs=tuple(int(c) for c in ctxs), tree=False)
+    say(f"[case] {len(rows)} ragged sequences, {int(rows.sum())} rows, kv={kv} S={S_}")
+    ref, lref = oracle.attention(w)
+    got, lse, flags, plan = run_ragged(w, S_, "f16")
+    n = w.total_rows
+    assert flags == 0
+    check_parity(got[:n], ref, "f16", f"150 sequences kv={kv} S={plan.info().num_splits if S_ == 0 else S_}")
+    assert np.abs(lse[:n] - lref).max() <= 2e-3
