@@ -11,17 +11,20 @@
 // The workgroup has 8 waves in two roles, one of each role per SIMD, so that
 // one wave's matrix-core work overlaps the other's vector work:
 //   score waves (rh, kh)   rows half rh, pages 2kh and 2kh + 1 of every
-//                          64-key tile: int8 -> fp16 dequant of K from LDS,
-//                          S^T = K Q^T on v_mfma_f32_16x16x32_f16 (keys on M,
-//                          rows on N, Q resident in registers), causal / tree /
+//                          64-key tile: S^T = K Q^T on v_mfma_f32_16x16x32_f16
+//                          (keys on M, rows on N, Q resident in registers);
+//                          8-bit K enters as its exact int8 codes, one MFMA
+//                          per 32-dim scale block, and the block scale is
+//                          applied to each fp32 block product; causal / tree /
 //                          page-tail mask, P = 2^(t - m_ref) in fp16 -> LDS.
 //   output waves q = 0..3  each owns head_dim quarter q: dequant of that
 //                          quarter of the tile's V, O^T += V^T P^T on the same
 //                          MFMA, with P of the previous tile read from LDS.
 //                          They also issue every LDS-DMA: page q of K (and its
 //                          scales), that quarter of V (and page q's scales).
-// Every KV element is therefore dequantised once per workgroup, and O lives
-// in exactly one wave, so the epilogue needs no cross-wave O reduction.
+// Every V element is therefore dequantised once per workgroup (K codes are
+// converted once per row half), and O lives in exactly one wave, so the
+// epilogue needs no cross-wave O reduction.
 //
 // Pipeline: separate K and V rings of R stages, filled by
 // global_load_lds_dwordx4 (no VGPR holds data in flight).  Iteration i: score
@@ -736,9 +739,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       const int rr = 16 * (NS * rh + nt) + n16;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        int dim0;
-        if constexpr (G::Q8) dim0 = 64 * (ks >> 1) + 16 * g4 + 8 * (ks & 1);
-        else dim0 = 32 * ks + 8 * g4;
+        // k-step ks covers dims [32 ks, 32 ks + 32): one 8-bit scale block
+        const int dim0 = 32 * ks + 8 * g4;
         qf[ks][nt] = *reinterpret_cast<const h16x8*>(q_unit(rr, dim0 >> 3));
       }
       const int r = rowbase + rr;
@@ -794,10 +796,14 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
             if constexpr (decltype(mk)::value) t = zval(u, nt, i, mk) - mre;
             else t = __builtin_fmaf(sacc[u][nt][i], c2, -mre);
             pv[i] = fast_exp2(t);
-            ls += pv[i];
           }
           const h16x4 ph = {(h16)pv[0], (h16)pv[1], (h16)pv[2], (h16)pv[3]};
           *LDS_PTR(h16x4, pb + (NS * rh + nt) * 1024 + (n16 + 16 * (2 * kh + u)) * 16) = ph;
+          // the row sum adds the fp16 weights P.V uses, so a row that one key
+          // dominates returns that key's V unscaled by P's rounding
+          const h16x2 one2 = {(h16)1.0f, (h16)1.0f};
+          ls = __builtin_amdgcn_fdot2(h16x2{ph[0], ph[1]}, one2, ls, false);
+          ls = __builtin_amdgcn_fdot2(h16x2{ph[2], ph[3]}, one2, ls, false);
         }
         lt[nt] = ls;
         lmx = fmaxf(lmx, ls);
@@ -828,51 +834,77 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
 #pragma unroll
           for (int nt = 0; nt < NS; ++nt) sacc[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (G::Q8) {
-          // per page: this lane's token scales, D/32 fp16 = D/64 dwords;
-          // chunk c uses block 2c + g/2, i.e. half (g/2) of dword c
-          uint32_t sw[2][D / 64];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const uint32_t sp = st + 4 * G::KPAGE + (2 * kh + u) * D + n16 * (D / 16);
-            if constexpr (D == 256) {
-              const u32x4 t = *LDS_PTR(u32x4, sp);
-              sw[u][0] = t[0]; sw[u][1] = t[1]; sw[u][2] = t[2]; sw[u][3] = t[3];
-            } else if constexpr (D == 128) {
-              const u32x2 t = *LDS_PTR(u32x2, sp);
-              sw[u][0] = t[0]; sw[u][1] = t[1];
-            } else {
-              sw[u][0] = *LDS_PTR(uint32_t, sp);
-            }
-          }
-          // the whole tile's K bytes for this wave in one burst of LDS reads,
-          // so one read latency is paid per tile rather than one per chunk
-          u32x4 raw_k[2][G::KCH];
+          // K stays exact: the int8 codes become fp16 integers (exact), and
+          // each k-step of 32 dims, one scale block, is its own MFMA from a
+          // zero accumulator; its fp32 result is multiplied by the block
+          // scale of each key and added to the score.  (Scaling the codes in
+          // fp16 first would round every K element to 11 bits, an error that
+          // grows with the score.)  Lane (g, m) of a k-step holds dims
+          // 8g .. 8g + 7 of the block for key m: 8 bytes of the 16-byte DMA
+          // slot (g', m) of chunk ks / 2 with g' = 2 (ks & 1) + g / 2.
+          constexpr int SW = D / 64;  // scale dwords of one token (D/32 fp16)
+          // this lane's output keys 4g .. 4g + 3 (MFMA rows) of each page: all
+          // their block scales
+          uint32_t ksc[2][4][SW];
 #pragma unroll
           for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int c = 0; c < G::KCH; ++c)
-              raw_k[u][c] = *LDS_PTR(u32x4, st + (2 * kh + u) * G::KPAGE + 1024 * c + 16 * lane);
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t sp = st + 4 * G::KPAGE + (2 * kh + u) * D + (4 * g4 + e) * (D / 16);
+              if constexpr (SW == 4) {
+                const u32x4 t = *LDS_PTR(u32x4, sp);
+                ksc[u][e][0] = t[0]; ksc[u][e][1] = t[1]; ksc[u][e][2] = t[2]; ksc[u][e][3] = t[3];
+              } else if constexpr (SW == 2) {
+                const u32x2 t = *LDS_PTR(u32x2, sp);
+                ksc[u][e][0] = t[0]; ksc[u][e][1] = t[1];
+              } else {
+                ksc[u][e][0] = *LDS_PTR(uint32_t, sp);
+              }
+            }
+          // the whole tile's K bytes for this wave in one burst of LDS reads,
+          // so one read latency is paid per tile rather than one per k-step
+          u32x2 raw_k[2][KSTEPS];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+              raw_k[u][ks] = *LDS_PTR(u32x2, st + (2 * kh + u) * G::KPAGE + 1024 * (ks >> 1) +
+                                                 16 * (16 * (2 * (ks & 1) + (g4 >> 1)) + n16) + 8 * (g4 & 1));
           // keep the burst together (the scheduler would otherwise sink each
           // read next to its use and wait for it there)
 #pragma unroll
           for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int c = 0; c < G::KCH; ++c) asm volatile("" : "+v"(raw_k[u][c]));
-          const uint32_t sel = (g4 >> 1) ? 0x03020302u : 0x01000100u;
+            for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" : "+v"(raw_k[u][ks]));
+          const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+          // per k-step: both pages' fragments, the 2 NS block products, then
+          // their scaled adds (the products are in flight while the next
+          // k-step's fragments are converted)
 #pragma unroll
-          for (int c = 0; c < G::KCH; ++c) {
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            h16x8 kf[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const u32x4 raw = raw_k[u][c];
-              const h16x2 d2 = as_h2(__builtin_amdgcn_perm(sw[u][c], sw[u][c], sel));
-              const h16x8 k0 = deq8(raw[0], raw[1], d2, d2, d2, d2);
-              const h16x8 k1 = deq8(raw[2], raw[3], d2, d2, d2, d2);
-#pragma unroll
-              for (int nt = 0; nt < NS; ++nt) {
-                sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[2 * c][nt], sacc[u][nt], 0, 0, 0);
-                sacc[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[2 * c + 1][nt], sacc[u][nt], 0, 0, 0);
-              }
+              h16x2 a, b, c, d;
+              i8x4_to_h(raw_k[u][ks][0], a, b);
+              i8x4_to_h(raw_k[u][ks][1], c, d);
+              kf[u] = cat(a, b, c, d);
             }
+            f32x4 r[2][NS];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int nt = 0; nt < NS; ++nt)
+                r[u][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[u], qf[ks][nt], zero4, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int nt = 0; nt < NS; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const h16x2 sc = as_h2(ksc[u][e][ks >> 1]);
+                  sacc[u][nt][e] = __builtin_fmaf((float)sc[ks & 1], r[u][nt][e], sacc[u][nt][e]);
+                }
           }
         } else {
 #pragma unroll

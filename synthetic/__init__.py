@@ -22,4 +22,7 @@ from .workloads import (  # noqa: F401
     chain_parent,
     mixed_lowering,
     new_kv_rows,
+    peaked,
+    rising_max,
+    late_dominant,
 )

@@ -342,6 +342,76 @@ def mixed_lowering(seed: int = 5, prefill=(100, 37), prefill_ctx=(1016, 1032),
                          kv_dtype="q8_0", seed=seed, permute=True, parent=np.concatenate(par), **kw)
 
 
+def _bf16_const(x: float) -> np.uint16:
+    return bf16_bits_from_f32(np.array([x], np.float32))[0]
+
+
+def _set_k_block(w: Workload, tok: np.ndarray, blk: int, dim: int, code: np.ndarray, d: float) -> None:
+    """Overwrite 8-bit K block `blk` of the tokens `tok` (positions in
+    sequence 0, every KV head): all codes 0 except `dim` (= code) and the
+    block scale d (an fp16 value)."""
+    pg = w.block_table[0, tok // PAGE]
+    sl = tok % PAGE
+    lo = 32 * blk
+    w.k_pool[pg, :, sl, lo:lo + 32] = 0
+    w.k_pool[pg, :, sl, dim] = np.asarray(code, np.int8)[:, None]
+    w.k_scale[pg, :, sl, blk] = np.float16(d)
+
+
+def peaked(ctx: int = 32768, gain: float = 4.0, seed: int = 2, **kw) -> Workload:
+    """The 8-bit headline shape with Q scaled by `gain`: scores of standard
+    deviation ~gain nats, so a few keys dominate each row and the running max
+    of the online softmax is raised throughout the context."""
+    return make_workload(f"peaked_g{gain:g}_q8_b16_h24_kv4_d256_ctx{ctx}", ctx_lens=[ctx], B=16, H=24, KVH=4,
+                         D=256, q_dtype="bf16", kv_dtype="q8_0", seed=seed, q_gain=gain, **kw)
+
+
+def rising_max(ctx: int = 32768, slope_log2: float = 0.375, seed: int = 21, **kw) -> Workload:
+    """8-bit headline shape whose scores rise along the context by `slope_log2`
+    (base-2 units) per token, the same for every row and query head: each
+    64-key tile lifts the running max by 64 * slope_log2 (24 at the default),
+    so the online softmax rescales its running sum and output over and over,
+    with the earlier keys still weighing in.
+
+    Construction (exact in the stored format): every query row has 16 in dims
+    0, 32 and 64 and small noise (0.05 N(0,1)) elsewhere; key j gets the
+    target score z_j = ln2 * slope_log2 * (j - ctx/2) nats split as
+    128 q0 + q1 + q2 / 128 over dims 0, 32, 64 of K blocks 0, 1, 2 with block
+    scales 128, 1 and 1/128 (every other code of those blocks is 0), so that
+    scale * q.k = z_j + noise.  Blocks 3.. and V are the usual N(0,1) data."""
+    w = make_workload(f"rising_max_s{slope_log2:g}_q8_b16_h24_kv4_d256_ctx{ctx}", ctx_lens=[ctx], B=16, H=24,
+                      KVH=4, D=256, q_dtype="bf16", kv_dtype="q8_0", seed=seed, permute=True, q_gain=0.05, **kw)
+    w.q[:, :, 0] = w.q[:, :, 32] = w.q[:, :, 64] = _bf16_const(16.0)
+    j = np.arange(ctx)
+    z = math.log(2.0) * slope_log2 * (j - ctx / 2)
+    q0 = np.floor(z / 128.0)
+    r = z - 128.0 * q0
+    q1 = np.floor(r)
+    q2 = np.floor((r - q1) * 128.0)
+    if np.abs(q0).max() > 127:
+        raise ValueError("slope too steep for the 8-bit construction at this context")
+    _set_k_block(w, j, 0, 0, q0.astype(np.int8), 128.0)
+    _set_k_block(w, j, 1, 32, q1.astype(np.int8), 1.0)
+    _set_k_block(w, j, 2, 64, q2.astype(np.int8), 1.0 / 128.0)
+    return w
+
+
+def late_dominant(ctx: int = 32768, margin: float = 13.0, seed: int = 23, **kw) -> Workload:
+    """8-bit headline shape with one key near the end of the context (56
+    tokens before the drafted rows, so in the last split of any split count
+    and visible to every row) whose score exceeds the others by about
+    `margin` nats for every row: every query row has 16 in dim 0, and that
+    key's K block 0 is zero but for code 127 in dim 0 with scale
+    margin / 127 (fp16).  It takes most of each row's weight, and the merge
+    must weigh the last split against all earlier ones."""
+    w = make_workload(f"late_dominant_q8_b16_h24_kv4_d256_ctx{ctx}", ctx_lens=[ctx], B=16, H=24, KVH=4, D=256,
+                      q_dtype="bf16", kv_dtype="q8_0", seed=seed, permute=True, **kw)
+    w.q[:, :, 0] = _bf16_const(16.0)
+    jd = np.array([ctx - w.B - 40])
+    _set_k_block(w, jd, 0, 0, np.array([127], np.int8), float(np.float16(margin / 127.0)))
+    return w
+
+
 def new_kv_rows(w: Workload, dtype: str = "f32", seed: int = 0):
     """K and V vectors for the B drafted rows of every sequence, as a KV append
     receives them: two arrays [num_seqs*B, KVH, D] of N(0,1) values in `dtype`

@@ -105,6 +105,15 @@ def bf16_rne(x):
     return r
 
 
+def check_bf16_twin(b16, f32, ref, what=""):
+    """A bf16 output checked through its fp32 twin (same call with fp32
+    output): the twin passes the 1e-3 / 2e-3 gate and the bf16 output is its
+    round-to-nearest-even, bit for bit."""
+    check_parity(f32, ref, "f32", f"{what} (fp32 twin)")
+    check_parity(b16, ref, "bf16", what)
+    assert np.array_equal(b16, bf16_rne(f32)), what
+
+
 def check_bf16_rounding(w, ref, num_splits):
     """bf16 output is exactly the rounded fp32 output; fp32 output passes the gate."""
     f32 = run_gpu(w, num_splits, "f32")[0]

@@ -70,6 +70,19 @@ def test_tiny_dense(S_, out_dtype):
     assert np.abs(lse - l).max() <= 1e-4 * max(1.0, np.abs(l).max())
     if out_dtype == "bf16":
         check_bf16_rounding(w, o, S_)
+    else:
+        # the case as specified: the oracle on the original fp32 K/V (the GPU
+        # reads them rounded to fp16, the pages' 16-bit KV format)
+        check_parity(got, tiny_f32_ref(), out_dtype, f"tiny S={S_} vs fp32 K/V")
+
+
+def tiny_f32_ref():
+    if "tiny_f32" not in _cache:
+        w32 = S.tiny_dense(kv_dtype="f32")
+        w16 = wl("tiny_f16")[0]
+        assert np.array_equal(w32.k_pool.astype(np.float16), w16.k_pool)  # same draws
+        _cache["tiny_f32"] = oracle.attention(w32)[0]
+    return _cache["tiny_f32"]
 
 
 @pytest.mark.parametrize("name", ["qwen_f16_d256", "qwen_f16_d128"])

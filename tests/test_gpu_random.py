@@ -18,7 +18,7 @@ import pytest
 import oracle
 import synthetic as S
 
-from .gpu_util import check_parity, ensure_lib, run_gpu, say
+from .gpu_util import check_bf16_twin, check_parity, ensure_lib, run_gpu, say
 from .test_gpu_ragged import run_ragged
 
 pytestmark = pytest.mark.gpu
@@ -88,5 +88,14 @@ def test_random_case(seed):
     assert flags == 0
     if got.size == 0:
         return  # no rows in the batch: nothing to compare, and no flag raised
-    check_parity(got, ref, w.out_dtype, f"random seed {seed}")
+    if w.out_dtype == "bf16":
+        # the same call with fp32 output: it passes the gate, and the bf16
+        # output is its round-to-nearest-even
+        if ragged:
+            twin = run_ragged(w, splits, "f32")[0][:w.total_rows]
+        else:
+            twin = run_gpu(w, splits, "f32")[0]
+        check_bf16_twin(got, twin, ref, f"random seed {seed}")
+    else:
+        check_parity(got, ref, w.out_dtype, f"random seed {seed}")
     assert np.abs(lse - lref).max() <= 2e-3
