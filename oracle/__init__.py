@@ -58,11 +58,14 @@ def _load():
                                            dp, ctypes.c_int]
         lib.orc_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, dp, dp, dp, dp, dp]
         lib.orc_f32_to_f16.argtypes = [ctypes.c_int64, vp, vp]
+        lib.orc_decode_f16.argtypes = [ctypes.c_int64, vp, vp]
+        lib.orc_decode_bf16.argtypes = [ctypes.c_int64, vp, vp]
         lib.orc_quantize_blocks.argtypes = [ctypes.c_int64, vp, vp, vp]
         lib.orc_append_kv.argtypes = [sp, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ip, ip]
         lib.orc_promote_kv.argtypes = [sp, ip, ip, ip, vp, vp, vp, vp, ip, ip, ip]
         for f in (lib.orc_attention, lib.orc_attention_items, lib.orc_split_partials, lib.orc_merge,
-                  lib.orc_f32_to_f16, lib.orc_quantize_blocks, lib.orc_append_kv, lib.orc_promote_kv):
+                  lib.orc_f32_to_f16, lib.orc_quantize_blocks, lib.orc_append_kv, lib.orc_promote_kv,
+                  lib.orc_decode_f16, lib.orc_decode_bf16):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -167,6 +170,24 @@ def merge(m: np.ndarray, l: np.ndarray, o: np.ndarray):
     if rc != 0:
         raise OracleError("merge rejected the inputs (rc=%d)" % rc)
     return out, lse
+
+
+def decode_f16(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> float64, by the oracle's decoder."""
+    lib = _load()
+    bits = np.ascontiguousarray(bits, np.uint16)
+    out = np.zeros(bits.shape, np.float64)
+    lib.orc_decode_f16(bits.size, _ptr(bits), _ptr(out))
+    return out
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, by the oracle's decoder."""
+    lib = _load()
+    bits = np.ascontiguousarray(bits, np.uint16)
+    out = np.zeros(bits.shape, np.float64)
+    lib.orc_decode_bf16(bits.size, _ptr(bits), _ptr(out))
+    return out
 
 
 def f32_to_f16(x: np.ndarray) -> np.ndarray:

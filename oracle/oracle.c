@@ -519,6 +519,16 @@ static void quantize_block(const float* x, int8_t* q, uint16_t* dbits) {
   *dbits = h;
 }
 
+int orc_decode_f16(int64_t n, const uint16_t* h, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f16_to_double(h[i]);
+  return ORC_OK;
+}
+
+int orc_decode_bf16(int64_t n, const uint16_t* b, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_double(b[i]);
+  return ORC_OK;
+}
+
 int orc_f32_to_f16(int64_t n, const float* x, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16_rne(x[i]);
   return ORC_OK;

@@ -112,6 +112,12 @@ int orc_split_partials(const orc_shape* p, const void* q, const void* k_pool,
 int orc_merge(int32_t nsplit, int64_t nrows, int32_t D, const double* m, const double* l,
               const double* o, double* out, double* lse);
 
+/* The oracle's own decoders of 16-bit inputs, exposed so that they can be
+ * checked bit pattern by bit pattern: IEEE binary16 (normal, subnormal, zero,
+ * inf, NaN) and bfloat16 bit patterns -> double (n values). */
+int orc_decode_f16(int64_t n, const uint16_t* h, double* out);
+int orc_decode_bf16(int64_t n, const uint16_t* b, double* out);
+
 /* fp32 -> IEEE binary16 bits, round to nearest even (n values). */
 int orc_f32_to_f16(int64_t n, const float* x, uint16_t* out);
 

@@ -114,6 +114,11 @@ def test_merge_of_any_partition_equals_direct(make, S_):
         b = _random_bounds(w, S_, rng)
         m, ll, oo = oracle.split_partials(w, b)
         mo, ml = oracle.merge(m, ll, oo)
+        if S_ == 1:
+            # one split is the direct path itself: weight exp(0) = 1, the same
+            # sums in the same order, so the merge reproduces it bit for bit
+            assert np.array_equal(mo.reshape(o.shape), o)
+            assert np.array_equal(ml.reshape(l.shape), l)
         assert _relerr(mo.reshape(o.shape), o) <= 1e-12
         assert np.abs(ml.reshape(l.shape) - l).max() <= 1e-12 * max(1.0, np.abs(l).max())
 
@@ -404,3 +409,70 @@ def test_generator_q8_roundtrip_and_tables():
         assert np.all(np.abs(kf - K) <= kd / 2 + 1e-12 * np.abs(kf))
     par = S.tree_parent(2, 8, np.random.default_rng(1))
     assert all(-1 <= par[i] < i for i in range(len(par)))
+
+
+# --------------------------------------------------------------------------
+# 16-bit decoders (every fp16 Q value, fp16 K/V value and 8-bit block scale
+# passes through the oracle's fp16 decoder; bf16 Q through its bf16 decoder)
+# --------------------------------------------------------------------------
+
+def test_fp16_decode_every_bit_pattern():
+    """All 65,536 binary16 patterns against numpy's float16 -> float64
+    conversion: zeros of both signs, every subnormal, normals, infinities
+    and NaNs."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode_f16(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))  # -0.0 stays -0.0
+    # the subnormal range in closed form: pattern m (1 <= m < 1024) is m * 2^-24
+    m = np.arange(1, 1024)
+    assert np.array_equal(got[m], m * 2.0 ** -24)
+    assert np.array_equal(got[0x8000 + m], -m * 2.0 ** -24)
+    assert got[0x7C00] == np.inf and got[0xFC00] == -np.inf
+
+
+def test_bf16_decode_every_bit_pattern():
+    """All 65,536 bfloat16 patterns against torch's bfloat16 -> float64
+    conversion."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_q8_decode_with_subnormal_and_extreme_scales():
+    """A one-key 8-bit context whose block scales are fp16 subnormals, the
+    smallest normal and the largest finite value: with Q = e_d (a one-hot
+    query) the attention output is that key's V, and the one-key score is
+    the decoded K element; both must equal scale * code in closed form."""
+    scales = np.array([1, 0x3FF, 0x400, 0x7BFF, 0x0001, 0x3C00, 0x8001, 0x5BFF], np.uint16)  # fp16 bit patterns
+    codes = np.array([127, -127, 1, -1, 64, -128, 3, 100], np.int8)
+    D = 256
+    w = S.make_workload("one_key", ctx_lens=[1], B=1, H=1, KVH=1, D=D, q_dtype="f32", kv_dtype="q8_0", seed=0)
+    w.k_pool[...] = 0
+    w.v_pool[...] = 0
+    w.k_scale[...] = np.float16(0)
+    for b in range(D // 32):
+        w.k_pool[0, 0, 0, 32 * b] = codes[b]
+        w.k_scale[0, 0, 0, b] = scales[b:b + 1].view(np.float16)[0]
+        w.v_pool[0, 0, 32 * b + 5, 0] = codes[b]
+        w.v_scale[0, 0, b, 0] = scales[b:b + 1].view(np.float16)[0]
+    exact = scales.view(np.float16).astype(np.float64) * codes.astype(np.float64)
+    o, lse = oracle.attention(w)
+    # one visible key: weight 1, output = V of that key
+    v = np.zeros(D)
+    v[32 * np.arange(D // 32) + 5] = exact
+    assert np.array_equal(o.reshape(D), v)
+    # the score of the single key is the lse: scale * sum_d q_d k_d, q one-hot on dim 32 b
+    for b in range(D // 32):
+        w.q[...] = 0
+        w.q[0, 0, 32 * b] = 1.0
+        o, lse = oracle.attention(w)
+        assert lse.reshape(())[()] == np.float64(np.float32(w.scale)) * exact[b]
