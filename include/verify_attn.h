@@ -179,6 +179,29 @@ va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool
                           void* stream);
 
 /*
+ * verify_attn_run without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The split partials live in a device array the
+ * library holds, one per GPU, for the life of the process (the first plan
+ * made for a device, or the first call on it, looks its address up);
+ * nothing is allocated, freed or cleared per call.
+ *   flags   device uint32, caller-owned, 4-byte aligned: the VA_FLAG_* bits of
+ *           the device-side metadata checks are ORed into it (zero it once;
+ *           it is never cleared by the library)
+ * Every other argument as for verify_attn_run.  Uniform plans only (ragged
+ * plans: VA_EINVAL).  Limit: S * num_seqs * B * H * (head_dim + 2) * 4 bytes
+ * of partials must fit the array's 64 MiB (16 sequences of the B = 16,
+ * H = 24, D = 256 shape at S = 64, for instance), else VA_EWORKSPACE and
+ * nothing is launched.  All calls on one GPU share the array: two calls that
+ * overlap in time on one GPU (different streams without ordering between
+ * them) race on it and may corrupt each other's outputs.
+ */
+va_status verify_attn_run_noalloc(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                  const void* k_scale, const void* v_scale, const int32_t* block_table,
+                                  const int32_t* ctx_lens, const int32_t* parent, int32_t num_splits, void* out,
+                                  float* lse, uint32_t* flags, void* stream);
+
+/*
  * Ragged rows: one call that mixes paged prefill segments, ordinary direct
  * rows and draft trees (page "perf(qwen35): retain speculation during paged
  * prefill", Mechanism: a step lowers [prefill segments][direct rows][tree

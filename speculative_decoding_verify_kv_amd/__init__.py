@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     verify_attn_read_flags,
     verify_attn_run,
     verify_attn_run_merge,
+    verify_attn_run_noalloc,
     verify_attn_run_partial,
     verify_attn_run_ragged,
     verify_attn_status_string,

@@ -64,7 +64,7 @@ _lib = None
 EXPORTED = (
     "verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_plan_destroy",
     "verify_attn_run", "verify_attn_run_ragged", "verify_attn_run_partial", "verify_attn_run_merge",
-    "verify_attn_append_kv",
+    "verify_attn_run_noalloc", "verify_attn_append_kv",
     "verify_attn_promote_kv", "verify_attn_promote_workspace_bytes", "verify_attn_read_flags",
     "verify_attn_status_string",
 )
@@ -94,6 +94,7 @@ def load(path: Optional[str] = None):
                                            vp]
     lib.verify_attn_run_partial.argtypes = run_args
     lib.verify_attn_run_merge.argtypes = [vp, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.verify_attn_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     lib.verify_attn_append_kv.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_promote_kv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.verify_attn_promote_workspace_bytes.argtypes = [vp]
@@ -103,7 +104,8 @@ def load(path: Optional[str] = None):
     lib.verify_attn_status_string.restype = ctypes.c_char_p
     for n in ("verify_attn_plan", "verify_attn_plan_for_cus", "verify_attn_plan_get_info", "verify_attn_run",
               "verify_attn_run_ragged",
-              "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_append_kv", "verify_attn_promote_kv",
+              "verify_attn_run_partial", "verify_attn_run_merge", "verify_attn_run_noalloc", "verify_attn_append_kv",
+              "verify_attn_promote_kv",
               "verify_attn_read_flags"):
         getattr(lib, n).restype = i32
     if path is None:
@@ -230,6 +232,16 @@ def verify_attn_run_merge(plan: Plan, num_splits, out, lse, workspace, workspace
                                       _stream(stream))
     if raise_on_error:
         _check(st, "verify_attn_run_merge")
+    return st
+
+
+def verify_attn_run_noalloc(plan: Plan, q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent,
+                            num_splits, out, lse, flags, stream=None, *, raise_on_error=True) -> int:
+    st = load().verify_attn_run_noalloc(plan.handle, _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                        _ptr(v_scale), _ptr(block_table), _ptr(ctx_lens), _ptr(parent),
+                                        int(num_splits), _ptr(out), _ptr(lse), _ptr(flags), _stream(stream))
+    if raise_on_error:
+        _check(st, "verify_attn_run_noalloc")
     return st
 
 

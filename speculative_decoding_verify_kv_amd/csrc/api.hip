@@ -12,11 +12,47 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "va_internal.h"
 
+// Device memory of verify_attn_run_noalloc: the split partials of a call live
+// here instead of in a caller workspace.  Each GPU the library runs on holds
+// its own copy for the life of the process; host code reaches it only through
+// the per-device address hipGetSymbolAddress returns (scratch_on_device).
+static __device__ __align__(256) char scratch[va::kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of `scratch` on the current device, looked up once per device.
+va_status scratch_on_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return VA_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VA_OK;
+}
+
+// The same at plan time, with `device` made current for the lookup.
+va_status scratch_setup(int device) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return VA_EHIP;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return VA_EHIP;
+  void* ptr = nullptr;
+  const va_status st = scratch_on_device(&ptr);
+  if (cur != device && hipSetDevice(cur) != hipSuccess) return VA_EHIP;
+  return st;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -215,6 +251,8 @@ va_status verify_attn_plan(const va_problem* problem, int32_t num_splits, int32_
   if (st != VA_OK) return st;
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device_ordinal) != hipSuccess) return VA_EHIP;
+  // set-up of verify_attn_run_noalloc's device memory on this device
+  if (scratch_setup(device_ordinal) != VA_OK) return VA_EHIP;
   return make_plan(problem, num_splits, prop.multiProcessorCount, out_plan, workspace_bytes);
 }
 
@@ -282,6 +320,46 @@ va_status verify_attn_run(const va_plan* plan, const void* q, const void* k_pool
   const va::PartialParams pp = partial_params(plan, a, S, out, lse, workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (va::launch_partial(pp, plan->prob.kv_dtype, plan->tiling.nt, s) != hipSuccess) return VA_EHIP;
+  if (S > 1 && va::launch_merge(merge_params(pp, out, lse), s) != hipSuccess) return VA_EHIP;
+  return VA_OK;
+}
+
+va_status verify_attn_run_noalloc(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                                  const void* k_scale, const void* v_scale, const int32_t* block_table,
+                                  const int32_t* ctx_lens, const int32_t* parent, int32_t num_splits, void* out,
+                                  float* lse, uint32_t* flags, void* stream) {
+  if (!plan || !flags || !aligned(flags, 4)) return VA_EINVAL;
+  if (ragged(plan->prob)) return VA_EINVAL;  // uniform plans only
+  const va_problem& p = plan->prob;
+  const int32_t S = num_splits ? num_splits : plan->num_splits;
+  if (S < 1 || S > va::kMaxSplits) return VA_EINVAL;
+  // split partials: fp32 O, m and l of S splits for every (row, head)
+  const size_t need = S > 1 ? (size_t)S * (size_t)rows_capacity(p) * p.num_q_heads * ((size_t)p.head_dim + 2) *
+                                  sizeof(float)
+                            : 0;
+  if (need > va::kScratchBytes) return VA_EWORKSPACE;
+  void* base = nullptr;
+  if (scratch_on_device(&base) != VA_OK) return VA_EHIP;
+  // check_run with a workspace stand-in: the scratch partials sized for S
+  va_plan local = *plan;
+  local.max_splits = S;
+  local.workspace_bytes = 0;
+  const RunArgs a{q, k_pool, v_pool, k_scale, v_scale, block_table, ctx_lens, parent, nullptr};
+  int32_t S_run = 0;
+  va_status st = check_run(&local, a, S, out, lse, base, 0, &S_run);
+  if (st != VA_OK) return st;
+  va::PartialParams pp = partial_params(&local, a, S, out, lse, base);
+  // partials start at the array's base (the header of a workspace is not
+  // needed: flag bits go to the caller's word)
+  const int64_t nrows = pp.nrows;
+  float* part = static_cast<float*>(base);
+  pp.part_o = part;
+  pp.part_m = part + (int64_t)S * nrows * p.head_dim;
+  pp.part_l = pp.part_m + (int64_t)S * nrows;
+  pp.part_n = nullptr;
+  pp.flags = flags;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (va::launch_partial(pp, p.kv_dtype, plan->tiling.nt, s) != hipSuccess) return VA_EHIP;
   if (S > 1 && va::launch_merge(merge_params(pp, out, lse), s) != hipSuccess) return VA_EHIP;
   return VA_OK;
 }

@@ -15,6 +15,8 @@ constexpr int kMaxSplits = 256;
 constexpr int kMaxRows = 64;         // B limit of a uniform plan (ancestry bitmask width)
 constexpr int kMaxRowsRagged = 4096; // per-sequence row limit of a ragged plan (chains past 64)
 constexpr size_t kHeaderBytes = 256; // workspace flag header
+// Device memory verify_attn_run_noalloc keeps its split partials in (per GPU)
+constexpr size_t kScratchBytes = (size_t)64 << 20;
 // Ragged calls: fewest pages a split of a sequence takes (two 64-token
 // tiles).  A sequence shorter than S such splits uses fewer splits, and the
 // rest of its workgroups exit at once.

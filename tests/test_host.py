@@ -315,3 +315,24 @@ def test_ragged_entry_checks(lib):
     assert promote_status(ragged) == va.VA_EINVAL
     assert va.load().verify_attn_run_ragged(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
                                             None, FAKE, 1 << 30, None) == va.VA_EINVAL
+
+
+def test_noalloc_host_rejections(lib):
+    """verify_attn_run_noalloc refuses, before any device call: a NULL flag
+    word, a ragged plan, and partials beyond its 64 MiB device array."""
+    import ctypes
+
+    fake = 1 << 20  # aligned non-NULL stand-ins (nothing is dereferenced on the host)
+    big = va.make_problem(num_seqs=64, rows_per_seq=16, num_q_heads=24, num_kv_heads=4, head_dim=256,
+                          num_pages=2048 * 64, max_pages_per_seq=2048, max_ctx=32768)
+    plan = va.verify_attn_plan_for_cus(big, 64, 256)
+    args = [plan.handle] + [fake] * 8 + [0, fake, fake]
+    assert lib.verify_attn_run_noalloc(*args, None, None) == va.VA_EINVAL  # no flag word
+    # 64 * 16 * 24 rows x 258 floats x 64 splits = 1.6 GB of partials
+    assert lib.verify_attn_run_noalloc(*args, fake, None) == va.VA_EWORKSPACE
+    # the direct path (S = 1) needs no partials at all, but still a device; a
+    # ragged plan is refused outright
+    rag = va.make_problem(num_seqs=2, rows_per_seq=8, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                          num_pages=64, max_pages_per_seq=32, max_ctx=512, max_total_rows=10)
+    rplan = va.verify_attn_plan_for_cus(rag, 4, 256)
+    assert lib.verify_attn_run_noalloc(rplan.handle, *([fake] * 8), 0, fake, fake, fake, None) == va.VA_EINVAL
