@@ -13,12 +13,17 @@ tree and the chain sweep B = 4, 8, 16, 32), one JSON line each, with the
 same cold-pool rotation; the default run prints only the headline line.
 
 Prints one JSON line.  value = KV bytes of the valid tokens / time per call
-(GB/s); roofline = the partial kernel's algorithmic KV bytes / its average
-duration (HIP events around back-to-back launches on the launch stream)
-against the 8 TB/s HBM peak, with the HBM traffic per launch measured by
-rocprofv3 counters (null once the kernel source differs from the profiled
-one) and the MFMA rate; cpu_baseline = the fp64 oracle timed on the host
-cores over a few full calls.
+(GB/s) over the K timed calls, after ~50 ms of untimed calls (the device
+clock takes a few milliseconds of load to settle) and the W warmup steps;
+us_per_call_median / _p95 are over the per-call times of 10-call groups.
+roofline = the partial kernel's algorithmic KV bytes / its average duration
+(HIP events around back-to-back launches on the launch stream) against the
+8 TB/s HBM peak, frac_call the same for the whole call, with the bytes per
+launch of the partial kernel (traffic) and of partial + merge (traffic_call)
+measured by rocprofv3 counters (null once a kernel source differs from the
+profiled one) and the MFMA rate; cpu_baseline = the fp64 oracle timed on the
+host cores (whole calls on the job's worker threads, and a sample on one
+thread).
 """
 
 from __future__ import annotations
@@ -40,23 +45,71 @@ NPOOLS = 8
 
 
 def traffic_from_profile(root):
-    """HBM bytes per partial launch from the committed counter summary, or None
-    when the partial kernel's source changed after the counters were taken."""
+    """HBM-side bytes per launch of the partial and the merge kernel from the
+    committed counter summary: {"partial": B, "merge": B}, or None when either
+    kernel's source changed after the counters were taken."""
     import hashlib
     import re
 
     prof = os.path.join(root, "profiles", "verify_partial_q8_b16_h24_kv4_d256_ctx32768_counters.md")
-    src = os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc", "verify_partial.hip")
+    csrc = os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc")
     try:
         text = open(prof).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digests = {k: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+                   for k, f in (("partial", "verify_partial.hip"), ("merge", "verify_merge.hip"))}
     except OSError:
         return None
-    m_sha = re.search(r"kernel_source_sha256: ([0-9a-f]{64})", text)
-    m_val = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not m_sha or not m_val or m_sha.group(1) != digest:
-        return None
-    return int(m_val.group(1))
+    out = {}
+    for k in ("partial", "merge"):
+        m_sha = re.search(rf"{k}_source_sha256: ([0-9a-f]{{64}})", text)
+        m_val = re.search(rf"{k}_traffic_bytes_per_launch: (\d+)", text)
+        if not m_sha or not m_val or m_sha.group(1) != digests[k]:
+            return None
+        out[k] = int(m_val.group(1))
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, kv_bytes, oracle):
+    """The fp64 oracle on the host cores, as it stands: the whole call on the
+    worker threads the box grants this job (at most 16) and a bounded sample
+    (one row-head in eight) on one thread, each the median of 3 timed runs,
+    scaled to whole-call KV GB/s."""
+    import statistics
+
+    rows = w.num_seqs * w.B
+    items = [(r // w.B, r % w.B, h) for r in range(rows) for h in range(w.H)]
+
+    def med(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    nthreads = oracle.default_threads()
+    t_all = med(lambda: oracle.attention(w, nthreads=nthreads))
+    sample = items[::8]
+    t_one = med(lambda: oracle.attention_items(w, sample, nthreads=1)) * len(items) / len(sample)
+    return {"value": round(kv_bytes / t_all / 1e9, 4), "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"whole calls of the same workload (all {len(items)} row-heads, ctx {int(w.ctx_lens[0])}), "
+                      f"median of 3, on {nthreads} worker threads",
+            "seconds_per_call": round(t_all, 4),
+            "single_thread": {"value": round(kv_bytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds_per_call": round(t_one, 3),
+                              "sample": f"{len(sample)} of the {len(items)} row-heads (every 8th), median of 3, "
+                                        "scaled to the whole call"},
+            "host_cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def parse():
@@ -67,6 +120,8 @@ def parse():
     # few milliseconds of calls ~10% slower.
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=2000)
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed calls for this long before the warmup steps (device clock to steady state)")
     ap.add_argument("--ctx", type=int, default=32768)
     ap.add_argument("--splits", type=int, default=0, help="0 = the plan's heuristic")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
@@ -316,6 +371,16 @@ def main():
         fn(plan, dev["q"], k, v, ks, vs, tables[i % args.pools], dev["ctx_lens"], None, 0, out, lse, ws,
            stream=stream)
 
+    # ---- untimed: bring the device clock to its steady loaded state (the
+    # first milliseconds of load after idle run ~10% slower), then the W
+    # warmup steps ----
+    t_settle = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(64):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -332,6 +397,22 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
     gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---- the same calls again in groups of GROUP back-to-back calls, an
+    # event between groups (an event after every call would itself add ~2 us
+    # per call): the per-call time of each group, median and 95th percentile
+    # over the groups ----
+    GROUP = 10
+    ngroups = max(1, args.steps // GROUP)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(ngroups + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for gidx in range(ngroups):
+        for j in range(GROUP):
+            step(gidx * GROUP + j)
+        evs[gidx + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([1e3 * evs[g].elapsed_time(evs[g + 1]) / GROUP for g in range(ngroups)])
 
     # ---- per-kernel durations on the launch stream: each kernel timed over
     # `steps` back-to-back launches between two events (the partial kernel
@@ -355,24 +436,16 @@ def main():
     flops = 4.0 * w.D * w.H * sum(int(c) - w.B + (i + 1) for c in w.ctx_lens for i in range(w.B))
     mfma_tflops = flops / (partial_avg_us * 1e-6) / 1e12
     flags = va.verify_attn_read_flags(plan, ws, stream)
+    traffic = traffic_from_profile(ROOT)
 
-    # ---- CPU baseline: the fp64 oracle on the host cores, one full call ----
+    # ---- CPU baseline: the fp64 oracle on the host cores ----
     cpu = None
     if not args.no_cpu:
         import oracle
 
-        nthreads = oracle.default_threads()
-        calls = 0
-        t0 = time.perf_counter()
-        while calls < 5 and (calls == 0 or time.perf_counter() - t0 < 1.5):
-            oracle.attention(w, nthreads=nthreads)
-            calls += 1
-        dt = (time.perf_counter() - t0) / calls
-        cpu = {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-               "sample": f"{calls} full calls of the same workload (all {w.num_seqs * w.B * w.H} row-heads, "
-                         f"ctx {args.ctx}), {dt:.2f} s wall each on {nthreads} threads",
-               "seconds_per_call": dt}
+        cpu = cpu_baseline(w, kv_bytes, oracle)
 
+    us_call = ms_per_step * 1e3
     rec = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -380,8 +453,11 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms_per_step,
-        "us_per_call": ms_per_step * 1e3,
+        "us_per_call": us_call,
+        "us_per_call_median": round(float(np.median(per_call)), 3),
+        "us_per_call_p95": round(float(np.percentile(per_call, 95)), 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -391,9 +467,12 @@ def main():
                    "kv": "q8_0", "q": "bf16", "out": "f16", "splits": S_used, "row_groups": info.row_groups,
                    "kv_pools_rotated": args.pools, "kv_bytes_per_call": kv_bytes},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(ROOT),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic["partial"] if traffic else None,
                      "kernel": "verify_partial_kernel<256,Q8,6,false>", "kernel_avg_us": round(partial_avg_us, 3),
                      "merge_avg_us": round(merge_avg_us, 3),
+                     "frac_call": round(kv_bytes / (us_call * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic_call": (traffic["partial"] + traffic["merge"]) if traffic else None,
                      "mfma": {"tflops": round(mfma_tflops, 1), "peak_tflops": MFMA_PEAK_TFLOPS,
                               "util": round(mfma_tflops / MFMA_PEAK_TFLOPS, 4)}},
         "cpu_baseline": cpu,

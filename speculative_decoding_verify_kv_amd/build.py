@@ -71,5 +71,45 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+def resource_report() -> str:
+    """Per-kernel register, scratch, LDS and occupancy figures the compiler
+    reports for the gfx950 code of every source (a markdown table)."""
+    import re
+
+    rows = []
+    with tempfile.TemporaryDirectory(prefix="va_res_") as tmp:
+        for src in SOURCES:
+            cmd = [hipcc(), *_flags(), *PER_SOURCE_FLAGS.get(src, []), "--cuda-device-only", "-c",
+                   os.path.join(CSRC, src), "-o", os.path.join(tmp, src + ".o"),
+                   "-Rpass-analysis=kernel-resource-usage"]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")
+            cur = None
+            for line in r.stderr.splitlines():
+                m = re.search(r"remark: Function Name: (\S+)", line)
+                if m:
+                    cur = {"src": src, "name": m.group(1)}
+                    rows.append(cur)
+                    continue
+                m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\S+) \[-Rpass", line)
+                if m and cur is not None:
+                    cur[m.group(1).strip()] = m.group(2)
+    names = subprocess.run(["c++filt"], input="\n".join(r["name"] for r in rows), capture_output=True,
+                           text=True).stdout.splitlines() if shutil.which("c++filt") else [r["name"] for r in rows]
+    out = ["| kernel | source | VGPR | AGPR | SGPR | VGPR spill | SGPR spill | scratch B/lane | LDS B/block |"
+           " waves/SIMD |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for r, n in zip(rows, names):
+        n = n.replace("va::(anonymous namespace)::", "").replace("(va::PartialParams)", "").replace(
+            "(va::MergeParams)", "").replace("(va::AppendParams)", "").replace("(va::PromoteParams)", "")
+        out.append(f"| `{n}` | {r['src']} | {r.get('VGPRs')} | {r.get('AGPRs')} | {r.get('TotalSGPRs')} | "
+                   f"{r.get('VGPRs Spill')} | {r.get('SGPRs Spill')} | {r.get('ScratchSize')} | {r.get('LDS Size')} | "
+                   f"{r.get('Occupancy')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if len(sys.argv) > 1 and sys.argv[1] == "--resources":
+        print(resource_report())
+    else:
+        print(build(verbose=True))
