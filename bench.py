@@ -302,6 +302,24 @@ def time_next_rows(args, torch, va, vdev, S):
          {"accepted_rows": n.tolist(), "flags": va.verify_attn_read_flags(plan, pws, stream)})
     del dev
 
+    # the paged batch of four 16-row sequences (contexts 1,016 / 1,024 / 1,032 /
+    # 40,000) as one ragged call: each sequence split by its own context
+    w = S.paged_ragged()
+    dev = vdev.to_device(w)
+    cu = torch.tensor([0, 16, 32, 48, 64], dtype=torch.int32, device="cuda")
+    plan = va.verify_attn_plan(vdev.problem_for(w, max_total_rows=64), 0, 0)
+    ws = vdev.workspace(plan)
+    out = torch.empty((64, w.H, w.D), dtype=torch.float16, device="cuda")
+    lse = torch.empty((64, w.H), dtype=torch.float32, device="cuda")
+    us = timed(lambda i: va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"],
+                                                   dev["v_scale"], dev["block_table"], dev["ctx_lens"], cu, None, 0,
+                                                   out, lse, ws, stream=stream), args.steps)
+    kv = w.kv_bytes_valid()
+    emit("paged 4 x B 16, ctx 1016/1024/1032/40000, as a ragged call (per-sequence splits)", w, us,
+         {"splits": plan.info().num_splits, "kv_bytes_per_call": kv, "GBps": round(kv / (us * 1e-6) / 1e9, 1),
+          "flags": va.verify_attn_read_flags(plan, ws, stream)})
+    del dev
+
     # ragged rows: prefill segments, direct rows and a tree in one call
     w = S.mixed_lowering()
     dev = vdev.to_device(w)

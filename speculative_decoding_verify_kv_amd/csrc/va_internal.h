@@ -17,10 +17,12 @@ constexpr int kMaxRowsRagged = 4096; // per-sequence row limit of a ragged plan 
 constexpr size_t kHeaderBytes = 256; // workspace flag header
 // Device memory verify_attn_run_noalloc keeps its split partials in (per GPU)
 constexpr size_t kScratchBytes = (size_t)64 << 20;
-// Ragged calls: fewest pages a split of a sequence takes (two 64-token
+// Ragged calls: fewest pages a split of a sequence takes (eight 64-token
 // tiles).  A sequence shorter than S such splits uses fewer splits, and the
-// rest of its workgroups exit at once.
-constexpr int kMinSplitPages = 8;
+// rest of its workgroups exit at once.  Longer minimum splits cost a short
+// sequence's rows some parallelism but save each split's fixed cost (Q
+// staging, partial write-back, a workgroup slot) and its partials.
+constexpr int kMinSplitPages = 32;
 
 // Kernel-side dtype codes (same values as va_dtype).
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kQ8 = 3 };

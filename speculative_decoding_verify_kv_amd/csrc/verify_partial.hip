@@ -300,19 +300,21 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // Workgroup -> (split, row group).  When every split has several row
   // groups, the row groups of one split get block ids 8 apart: blocks are
   // dealt round-robin to the 8 XCDs, so they share one L2 and run together.
-  // Ragged calls (SQ) take the grid as (row group, KV head, split counted
-  // down).  The row groups of all sequences are numbered in sequence order
+  // Ragged calls (SQ) take the grid as (split counted down, row group, KV
+  // head).  The row groups of all sequences are numbered in sequence order
   // (sequence s has ceil(rows_s * G / QROWS) of them), so no workgroup is
   // spent on a group a sequence does not have; each wave finds its sequence
   // with a prefix sum of those counts over cu_rows, 64 sequences at a time.
-  // Blocks go out in grid order, so the high splits, which only long
-  // sequences fill, start first and the short sequences' few splits fill in
-  // behind.
+  // The splits of one (row group, KV head) have consecutive block ids, and
+  // blocks are dealt round-robin to the 8 XCDs, so a long sequence's splits
+  // spread over all of them: with the row group fastest, four one-group
+  // sequences over 4 KV heads put every split of a sequence on two XCDs
+  // (the paged four-sequence batch ran 141 us that way, 78 us this way).
   int s, kvh, split, rg;
   if constexpr (SQ) {
-    kvh = blockIdx.y;
-    split = p.S - 1 - (int)blockIdx.z;
-    const int g = blockIdx.x;
+    split = p.S - 1 - (int)blockIdx.x;
+    const int g = blockIdx.y;
+    kvh = blockIdx.z;
     s = -1;
     rg = 0;
     int before = 0;
@@ -1188,7 +1190,7 @@ static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
     const int64_t bound = ((int64_t)p.total_rows * p.G + (int64_t)p.num_seqs * (QR - 1)) / QR;
     const int64_t groups = bound < all ? (bound > 1 ? bound : 1) : all;
     hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>),
-                       dim3((unsigned)groups, (unsigned)p.KVH, (unsigned)p.S),
+                       dim3((unsigned)p.S, (unsigned)groups, (unsigned)p.KVH),
                        dim3(kBlockThreads), 0, stream, p);
   }
   else

@@ -109,10 +109,13 @@ def test_long_prefill_segment(S_):
 @pytest.mark.parametrize("S_", [1, 8])
 def test_uniform_rows_through_ragged_entry_bitwise(S_):
     # B rows per sequence written as cu_rows = [0, B, 2B, ...]: the same plan
-    # shape and split count must give the same bits as verify_attn_run
+    # shape and split count must give the same bits as verify_attn_run.  The
+    # contexts are long enough (>= 8 splits of 32 pages) that the ragged rule
+    # (a sequence's splits hold at least 32 pages) cuts the same splits as
+    # the uniform one; shorter sequences take fewer, longer splits there.
     import torch
 
-    w = S.paged_ragged(ctxs=(1016, 1024, 1032, 3000))
+    w = S.paged_ragged(ctxs=(4096, 4112, 5000, 6000))
     wr = copy.deepcopy(w)
     wr.cu_rows = np.arange(0, w.num_seqs * w.B + 1, w.B, dtype=np.int32)
     say(f"[case] uniform via ragged S={S_}")
@@ -248,7 +251,7 @@ def test_longest_prefill_segment(S_):
 @pytest.mark.parametrize("S_", [64, 256])
 def test_short_sequences_leave_their_extra_splits(S_):
     """Ragged calls split each sequence by its own context into splits of at
-    least 8 pages: contexts of 17, 130 and 4,000 tokens fill 1, 2 and 32 of
+    least 32 pages: contexts of 17, 130 and 4,000 tokens fill 1, 1 and 8 of
     the S splits, and the workgroups of the other splits write nothing.  The
     partial area of the workspace is filled with NaN bytes first, so the
     merge reading any split that was not written would show."""
