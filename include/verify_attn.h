@@ -45,7 +45,14 @@
  *   lse         [num_seqs*B, H]               f32, optional (NULL = not written)
  *   Q8_0: each KV element is int8 q with value scale * q, one f16 scale per
  *   32 consecutive head_dim indices of one (token, KV head).  Token j of
- *   sequence s lives in page block_table[s][j / 16], slot j % 16.
+ *   sequence s lives in page block_table[s][j / 16], slot j % 16.  K enters
+ *   the score product exactly (codes as fp16 integers, the block scale
+ *   applied to the fp32 product of each 32-dim block).  V is formed as
+ *   scale * q in fp16 for the P.V product, so every V value must lie within
+ *   fp16's range, |scale * q| <= 65504: a V block scale of 516 or more (or of
+ *   512 or more with a code of -128) overflows there and makes the rows that
+ *   see it NaN.  The library's own quantiser (verify_attn_append_kv) gives
+ *   such scales only for values beyond fp16's range (max|x| > 65,500).
  *   The V page is stored dim-major because the P.V contraction reduces over
  *   tokens: that way a matrix-core operand (8 consecutive tokens of one
  *   dimension) is one contiguous load.

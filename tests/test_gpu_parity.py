@@ -355,3 +355,38 @@ def test_max_rows_and_splits(S_):
         assert info.num_splits == S_ or S_ == 0
     check_parity(got, o, "f16", f"B=64 S={S_} ({info.row_groups} row groups)")
     assert np.abs(lse - l).max() <= 2e-3
+
+
+def test_q8_large_magnitude_blocks():
+    """Large 8-bit block scales.  V: every V scale times 2^13 (values up to
+    ~36,000, inside fp16's range, which V = scale * code must respect) scales
+    the fp32 output by exactly 2^13, bit for bit, and the result meets the
+    gate relative to the output's size.  K: every K scale times 16 makes the
+    scores 16 times larger (attention as peaked as Q gain 16); K is applied
+    exactly (codes as fp16 integers, scale on the fp32 block product), so
+    the result meets the gate."""
+    import dataclasses
+
+    base = S.q8_long(ctx=4096)
+    say("[case] q8 large-magnitude blocks")
+    o_base, _ = oracle.attention(base)
+    g_base = run_gpu(base, 0, "f32")[0]
+    check_parity(g_base, o_base, "f32", "q8 4096 base")
+    k = 8192.0
+    wv = dataclasses.replace(base, v_scale=(base.v_scale.astype(np.float32) * k).astype(np.float16))
+    assert np.isfinite(wv.v_scale.astype(np.float32)).all()
+    assert float(np.abs(wv.v_scale.astype(np.float32)).max()) * 127 < 65504
+    o_v, _ = oracle.attention(wv)
+    got_v, lse_v, flags, _ = run_gpu(wv, 0, "f32")
+    assert flags == 0
+    assert np.array_equal(got_v, g_base * k)  # power-of-two scaling is exact end to end
+    rel, mx = errors(got_v, o_v)
+    say(f"  V x 2^13: rel_l2={rel:.3e} max_abs={mx:.3e} (max|out| {np.abs(o_v).max():.3e})")
+    assert rel <= 1e-3 and mx <= 2e-3 * k
+    wk = dataclasses.replace(base, k_scale=(base.k_scale.astype(np.float32) * 16).astype(np.float16))
+    o_k, l_k = oracle.attention(wk)
+    for out_dtype in ("f32", "f16"):
+        got_k, lse_k, flags, _ = run_gpu(wk, 0, out_dtype)
+        assert flags == 0
+        check_parity(got_k, o_k, out_dtype, f"q8 4096 K scales x16 ({out_dtype})")
+        assert np.abs(lse_k - l_k).max() <= 1e-4 * max(1.0, np.abs(l_k).max())
