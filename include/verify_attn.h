@@ -93,15 +93,15 @@
 extern "C" {
 #endif
 
-typedef enum {
-  VA_OK = 0,
-  VA_EINVAL = -1,
-  VA_EUNSUPPORTED = -2,
-  VA_EWORKSPACE = -3,
-  VA_EHIP = -4
-} va_status;
+/* Status and dtype codes are plain 32-bit integers across the ABI (the enums
+ * only name their values), so a caller may pass any value: an unknown dtype
+ * is refused (VA_EUNSUPPORTED in a va_problem, VA_EINVAL as the new_dtype of
+ * verify_attn_append_kv) and an unknown status reads "unknown status". */
+typedef int32_t va_status;
+enum { VA_OK = 0, VA_EINVAL = -1, VA_EUNSUPPORTED = -2, VA_EWORKSPACE = -3, VA_EHIP = -4 };
 
-typedef enum { VA_F32 = 0, VA_F16 = 1, VA_BF16 = 2, VA_Q8_0 = 3 } va_dtype;
+typedef int32_t va_dtype;
+enum { VA_F32 = 0, VA_F16 = 1, VA_BF16 = 2, VA_Q8_0 = 3 };
 
 /* Device flag bits (workspace header, read with verify_attn_read_flags). */
 #define VA_FLAG_BAD_CTX 0x1u    /* ctx_lens[s] < B, > max_ctx, or beyond the block table */

@@ -21,7 +21,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c (the sanitizer build of
+# tests/run_sanitized.py), which is loaded as it is and never rebuilt.
+_LIB_ENV = os.environ.get("ORACLE_LIB")
+_LIB_PATH = _LIB_ENV or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _DT = {"f32": 0, "f16": 1, "bf16": 2, "q8_0": 3}
@@ -29,6 +32,10 @@ _DT = {"f32": 0, "f16": 1, "bf16": 2, "q8_0": 3}
 
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so (portable x86-64, -O2)."""
+    if _LIB_ENV:
+        if not os.path.exists(_LIB_ENV):
+            raise RuntimeError(f"ORACLE_LIB={_LIB_ENV} does not exist")
+        return _LIB_ENV
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",

@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libverify_attn.so")
+# VERIFY_ATTN_LIB names another build of the same library (the host-sanitizer
+# build of tests/run_sanitized.py); the default is the in-tree build.
+LIB_PATH = os.environ.get("VERIFY_ATTN_LIB") or os.path.join(HERE, "libverify_attn.so")
 
 VA_OK, VA_EINVAL, VA_EUNSUPPORTED, VA_EWORKSPACE, VA_EHIP = 0, -1, -2, -3, -4
 VA_F32, VA_F16, VA_BF16, VA_Q8_0 = 0, 1, 2, 3
