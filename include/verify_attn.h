@@ -55,11 +55,16 @@
  *   such scales only for values beyond fp16's range (max|x| > 65,500).
  *   The V page is stored dim-major because the P.V contraction reduces over
  *   tokens: that way a matrix-core operand (8 consecutive tokens of one
- *   dimension) is one contiguous load.
+ *   dimension) is one contiguous load.  This departs from a token-major V
+ *   cache (V laid out like K): a caller holding one transposes each 16-slot
+ *   V page and its scales once when writing it; verify_attn_append_kv writes
+ *   drafted rows in this layout.
  *
  * OWNERSHIP AND STREAMS
  *   The caller owns every device buffer and the stream.  The library never
- *   allocates device memory, never synchronises inside verify_attn_run, and
+ *   allocates device memory per call (its one device allocation is the
+ *   64 MiB file-scope array behind verify_attn_run_noalloc, created with the
+ *   code object on each device), never synchronises inside verify_attn_run, and
  *   enqueues its kernels asynchronously on `stream` (a hipStream_t; NULL is the
  *   null stream).  A plan is immutable host memory owned by the library until
  *   verify_attn_plan_destroy; it may be shared across threads and streams.
@@ -73,7 +78,12 @@
  *   once after allocating it; the flags stay set until verify_attn_read_flags
  *   clears them.
  *
- * ERRORS (fail closed: nothing is launched on any error)
+ * ERRORS (fail closed: nothing is launched on any error; page "perf(gfx1100):
+ * speed up long-context DFlash verify 13.4% with FA2 split-KV and retain
+ * HipGraph/Redline PM4", Default and admission policy: unsupported shapes and
+ * resources that are not ready fail closed instead of running; Maintainer-
+ * review follow-up: the caller-owned partial workspace is part of admission,
+ * here VA_EWORKSPACE)
  *   VA_EUNSUPPORTED  shape or dtype outside what the kernels implement
  *   VA_EINVAL        NULL or misaligned (16 B) required pointer, bad argument
  *   VA_EWORKSPACE    workspace smaller than the plan needs, or num_splits
@@ -145,7 +155,13 @@ typedef struct {
 } va_plan_info;
 
 /*
- * Validate `problem`, choose the split count and size the workspace.
+ * Validate `problem`, choose the split count and size the workspace: the
+ * admission step (page "perf(gfx1100): speed up long-context DFlash verify
+ * 13.4% with FA2 split-KV and retain HipGraph/Redline PM4", Default and
+ * admission policy: shape, dtype and context admission at the boundary;
+ * Maintainer-review follow-up: the partial workspace is sized and checked as
+ * part of admission).  The pages fix S = 8 for their part; here S follows the
+ * device's CU count and max_ctx.
  *   problem          (host) copied into the plan
  *   num_splits       0 = choose from the device's CU count and max_ctx; else the
  *                    split count to size for (1..256)
@@ -162,15 +178,22 @@ va_status verify_attn_plan(const va_problem* problem, int32_t num_splits, int32_
 va_status verify_attn_plan_for_cus(const va_problem* problem, int32_t num_splits, int32_t num_cus,
                                    va_plan** out_plan, size_t* workspace_bytes);
 
-/* Fill `info` (host) from a plan. */
+/* Fill `info` (host) from a plan: the split count, row grouping and
+ * workspace size admission chose.  VA_EINVAL if either pointer is NULL. */
 va_status verify_attn_plan_get_info(const va_plan* plan, va_plan_info* info);
 
+/* Free a plan (host memory only; NULL is a no-op).  The caller must not
+ * destroy a plan while another thread is using it. */
 void verify_attn_plan_destroy(va_plan* plan);
 
 /*
  * Run the whole verify attention: the partial kernel, then (num_splits > 1)
  * the merge kernel; with one split the partial kernel writes out / lse
- * directly (the "direct" path).
+ * directly (the "direct" path).  Page "perf(gfx1100): speed up long-context
+ * DFlash verify 13.4% with FA2 split-KV and retain HipGraph/Redline PM4":
+ * Summary (split-KV verify of the drafted rows over the Q8 cache, partials
+ * in a caller-owned workspace); Performance, batch-16 kernel screen (partial
+ * and merge launches; one split is the direct path).
  *   num_splits  0 = the plan's choice; else 1..max_splits
  *   workspace   device buffer of at least the plan's workspace_bytes
  * Pointers as in MEMORY LAYOUTS; k_scale / v_scale must be NULL unless
@@ -317,10 +340,18 @@ va_status verify_attn_promote_kv(const va_plan* plan, const int32_t* accepted, c
 size_t verify_attn_promote_workspace_bytes(const va_plan* plan);
 
 /* Copy the workspace flag word to *flags (host) after synchronising `stream`,
- * then clear it on the device.  For tests and debugging; it blocks. */
+ * then clear it on the device.  For tests and debugging; it blocks.  The
+ * flag word is this library's device-side counterpart of fail-closed
+ * admission (page "perf(gfx1100): speed up long-context DFlash verify 13.4%
+ * with FA2 split-KV and retain HipGraph/Redline PM4", Default and admission
+ * policy): metadata that only the device sees (ctx_lens, block_table,
+ * parent) cannot be checked before launch, so a bad value is reported here
+ * and its rows are NaN.  VA_EINVAL on a NULL argument, VA_EHIP if a copy
+ * fails. */
 va_status verify_attn_read_flags(const va_plan* plan, void* workspace, void* stream, uint32_t* flags);
 
-/* Static description of a status code. */
+/* Static description of a status code (any int32; unknown codes read
+ * "unknown status").  The string is owned by the library. */
 const char* verify_attn_status_string(va_status status);
 
 #ifdef __cplusplus
