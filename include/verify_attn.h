@@ -72,11 +72,12 @@
  *
  * WORKSPACE
  *   verify_attn_plan reports workspace_bytes.  The first 256 bytes hold a
- *   uint32 flag word (kernels OR error bits into it); the rest holds the fp32
- *   split partials and, last, one int32 per (row, head): the number of splits
- *   that hold keys of the row's sequence (ragged calls).  Zero the workspace
- *   once after allocating it; the flags stay set until verify_attn_read_flags
- *   clears them.
+ *   uint32 flag word (kernels OR error bits into it); then the fp32 split
+ *   partials and one int32 per (row, head): the number of splits that hold
+ *   keys of the row's sequence (ragged calls); a ragged plan's workspace ends
+ *   with the call's work list (what verify_attn_run_ragged's first kernel
+ *   writes for the other two).  Zero the workspace once after allocating it;
+ *   the flags stay set until verify_attn_read_flags clears them.
  *
  * ERRORS (fail closed: nothing is launched on any error; page "perf(gfx1100):
  * speed up long-context DFlash verify 13.4% with FA2 split-KV and retain
@@ -250,12 +251,19 @@ va_status verify_attn_run_noalloc(const va_plan* plan, const void* q, const void
  *            more than 64 rows must be a chain (parent[i] == i - 1).
  * Every other argument as for verify_attn_run.  A sequence's outputs depend
  * only on its own rows, context and pages and on the plan and num_splits.
+ * The call runs three kernels: a one-workgroup pass that lists the call's
+ * work from cu_rows and ctx_lens (each sequence split by its own context,
+ * longest work first, packed densely so the workgroups spread evenly over
+ * the device), the partial kernel over that list, and the merge.  A plan
+ * with num_splits = 0 sizes S for one sequence at max_ctx plus num_seqs - 1
+ * sequences of up to 64 pages running as one wave of workgroups.
+ * Limits: num_seqs <= 2048 and num_kv_heads <= 256 (VA_EUNSUPPORTED).
  * A bad cu_rows entry sets VA_FLAG_BAD_ROWS; that sequence writes nothing
- * (outputs of rows it would own are unspecified).  Sequences before the first
- * bad entry are unaffected; where a bad entry makes later sequences' rows
- * overlap earlier ones, those later sequences may be left unwritten too
- * (the grid holds row groups for max_total_rows rows).  The grid is fixed by the
- * plan, so the call can be captured in a graph with live cu_rows.
+ * (outputs of rows it would own are unspecified).  Sequences are taken in
+ * order while their rows fit max_total_rows and their work fits the grid;
+ * where bad entries make sequences' rows overlap, the sequences past that
+ * point are left unwritten (their rows unspecified).  The grid is fixed by
+ * the plan, so the call can be captured in a graph with live cu_rows.
  */
 va_status verify_attn_run_ragged(const va_plan* plan, const void* q, const void* k_pool, const void* v_pool,
                                  const void* k_scale, const void* v_scale, const int32_t* block_table,

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libverify_attn.so")
-SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip", "append_kv.hip", "promote_kv.hip"]
+SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip", "ragged_schedule.hip", "append_kv.hip",
+           "promote_kv.hip"]
 # The partial kernel keeps its O accumulators in VGPRs and lets the Q operand
 # fragments sit in AGPRs (MFMA reads A/B from AGPRs); the default heuristic
 # instead shuttles the accumulators through AGPR spill slots every iteration.
@@ -101,7 +102,7 @@ def resource_report() -> str:
            " waves/SIMD |", "|---|---|---|---|---|---|---|---|---|---|"]
     for r, n in zip(rows, names):
         n = n.replace("va::(anonymous namespace)::", "").replace("(va::PartialParams)", "").replace(
-            "(va::MergeParams)", "").replace("(va::AppendParams)", "").replace("(va::PromoteParams)", "")
+            "(va::MergeParams)", "").replace("(va::ScheduleParams)", "").replace("(va::AppendParams)", "").replace("(va::PromoteParams)", "")
         out.append(f"| `{n}` | {r['src']} | {r.get('VGPRs')} | {r.get('AGPRs')} | {r.get('TotalSGPRs')} | "
                    f"{r.get('VGPRs Spill')} | {r.get('SGPRs Spill')} | {r.get('ScratchSize')} | {r.get('LDS Size')} | "
                    f"{r.get('Occupancy')} |")

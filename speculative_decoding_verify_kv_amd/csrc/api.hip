@@ -83,6 +83,9 @@ va_status check_problem(const va_problem* p) {
   if (p->max_ctx < p->rows_per_seq) return VA_EINVAL;
   if ((int64_t)p->max_ctx > (int64_t)p->max_pages_per_seq * va::kPage) return VA_EINVAL;
   if (rows_capacity(*p) * p->num_q_heads > INT32_MAX) return VA_EUNSUPPORTED;
+  // ragged calls list their work per sequence (sequence, KV head and split
+  // packed with the row group in 8-byte entries)
+  if (ragged(*p) && (p->num_seqs > va::kMaxSchedSeqs || p->num_kv_heads > 256)) return VA_EUNSUPPORTED;
   return VA_OK;
 }
 
@@ -94,12 +97,20 @@ va_status check_problem(const va_problem* p) {
 // fewest splits with that many tiles, since each split also writes fp32
 // partials that the merge reads back.  A ragged plan mixes prefill segments,
 // short decoders and long ones in one call: it is sized for one long decode
-// sequence (one row group) filling the CUs, and its shorter sequences keep
-// to fewer splits by themselves (kMinSplitPages).
+// sequence (one row group) filling the CUs left after two minimum-size
+// splits (kMinSplitPages) per KV head for each of the other num_seqs - 1
+// sequences (at most half the CUs are kept back), so a long sequence and
+// short ones of up to 64 pages each run as one wave of workgroups.  Each
+// sequence's splits still follow from its own context, the plan and the
+// call's split count only.
 int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
   const int64_t units = ragged(p) ? (int64_t)p.num_kv_heads
                                   : (int64_t)p.num_seqs * p.num_kv_heads * t.row_groups;
-  const int64_t s0 = std::max<int64_t>(1, cus / units);
+  int64_t room = cus;
+  if (ragged(p))
+    room -= std::min<int64_t>((int64_t)cus / 2,
+                              (int64_t)(p.num_seqs - 1) * p.num_kv_heads * 2 /* two minimum splits each */);
+  const int64_t s0 = std::max<int64_t>(1, room / units);
   const int64_t npages = ceil_div(p.max_ctx, va::kPage);
   const int64_t tiles = std::max<int64_t>(2, ceil_div(npages, 4 * s0));
   int64_t S = ceil_div(npages, 4 * tiles);
@@ -108,8 +119,37 @@ int32_t heuristic_splits(const va_problem& p, const va::Tiling& t, int cus) {
   return (int32_t)S;
 }
 
-size_t workspace_for(const va_problem& p, int S) {
+// Ragged calls: entries of the work list a call with S splits can have,
+// S * groups * KVH, where groups bounds sum_s ceil(rows_s * G / QROWS) over
+// sequences whose rows sum to at most the packed capacity.
+int64_t ragged_item_cap(const va_problem& p, const va::Tiling& t, int S) {
+  const int64_t QR = 16 * t.nt;
+  const int64_t all = (int64_t)p.num_seqs * t.row_groups;
+  const int64_t bound =
+      ((int64_t)p.max_total_rows * (p.num_q_heads / p.num_kv_heads) + (int64_t)p.num_seqs * (QR - 1)) / QR;
+  const int64_t groups = std::max<int64_t>(1, std::min(bound, all));
+  return (int64_t)S * groups * p.num_kv_heads;
+}
+
+// Workspace: the flag header; with S > 1 the fp32 partials (O, m, l) of S
+// splits for every (row, head) and one int32 per (row, head); for a ragged
+// plan then, 256-byte aligned, the work list: two int32 counts (16 bytes),
+// the packed rows to merge (one int32 each, padded to 16 bytes) and the
+// entries (8 bytes each).
+size_t sched_offset(const va_problem& p, int S) {
   const size_t nrows = (size_t)rows_capacity(p) * p.num_q_heads;
+  if (S <= 1) return va::kHeaderBytes;
+  const size_t end =
+      va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float) + nrows * sizeof(int32_t);
+  return (end + 255) & ~(size_t)255;
+}
+
+size_t merge_rows_bytes(const va_problem& p) { return ((size_t)rows_capacity(p) * sizeof(int32_t) + 15) & ~(size_t)15; }
+
+size_t workspace_for(const va_problem& p, const va::Tiling& t, int S) {
+  const size_t nrows = (size_t)rows_capacity(p) * p.num_q_heads;
+  if (ragged(p))
+    return sched_offset(p, S) + 16 + merge_rows_bytes(p) + (size_t)ragged_item_cap(p, t, S) * sizeof(int2);
   if (S <= 1) return va::kHeaderBytes;
   return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float) + nrows * sizeof(int32_t);
 }
@@ -132,8 +172,12 @@ va_status make_plan(const va_problem* problem, int32_t num_splits, int32_t cus, 
   plan->num_cus = cus;
   plan->num_splits = num_splits ? num_splits : heuristic_splits(p, t, cus);
   plan->max_splits = plan->num_splits;
+  if (ragged(p) && (t.row_groups >= 65536 || ragged_item_cap(p, t, plan->max_splits) > INT32_MAX)) {
+    delete plan;
+    return VA_EUNSUPPORTED;
+  }
   plan->scale = p.scale > 0.f ? p.scale : 1.0f / sqrtf((float)p.head_dim);
-  plan->workspace_bytes = workspace_for(p, plan->max_splits);
+  plan->workspace_bytes = workspace_for(p, t, plan->max_splits);
   *out_plan = plan;
   if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;
   return VA_OK;
@@ -202,6 +246,12 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
   pp.part_l = pp.part_m + (int64_t)plan->max_splits * nrows;
   // ragged calls split each sequence by its own context (see kMinSplitPages)
   pp.part_n = ragged(p) ? reinterpret_cast<int32_t*>(pp.part_l + (int64_t)plan->max_splits * nrows) : nullptr;
+  if (ragged(p)) {
+    char* sched = ws + sched_offset(p, plan->max_splits);
+    pp.item_count = reinterpret_cast<const int32_t*>(sched);
+    pp.items = reinterpret_cast<const int2*>(sched + 16 + merge_rows_bytes(p));
+    pp.item_cap = (int32_t)ragged_item_cap(p, plan->tiling, S);
+  }
   pp.num_seqs = p.num_seqs;
   pp.B = p.rows_per_seq;
   pp.total_rows = (int32_t)rows_capacity(p);
@@ -231,7 +281,13 @@ va::MergeParams merge_params(const va::PartialParams& pp, void* out, float* lse)
   mp.part_n = pp.part_n;
   mp.out = out;
   mp.lse = lse;
-  mp.live_rows = pp.cu_rows ? pp.cu_rows + pp.num_seqs : nullptr;
+  if (pp.items) {
+    mp.merge_count = pp.item_count + 1;
+    mp.merge_rows = pp.item_count + 4;
+  } else {
+    mp.merge_rows = nullptr;
+    mp.merge_count = nullptr;
+  }
   mp.heads = pp.H;
   mp.S = pp.S;
   mp.D = pp.D;
@@ -375,7 +431,26 @@ va_status verify_attn_run_ragged(const va_plan* plan, const void* q, const void*
   va_status st = check_run(plan, a, num_splits, out, lse, workspace, workspace_bytes, &S);
   if (st != VA_OK) return st;
   const va::PartialParams pp = partial_params(plan, a, S, out, lse, workspace);
+  // the work list first: the partial kernel's entries and the merge's rows
+  va::ScheduleParams sp;
+  sp.cu_rows = cu_rows;
+  sp.ctx_lens = ctx_lens;
+  sp.count = const_cast<int32_t*>(pp.item_count);
+  sp.items = const_cast<int2*>(pp.items);
+  sp.merge_rows = const_cast<int32_t*>(pp.item_count) + 4;
+  sp.flags = pp.flags;
+  sp.num_seqs = pp.num_seqs;
+  sp.B = pp.B;
+  sp.total_rows = pp.total_rows;
+  sp.G = pp.G;
+  sp.qrows = pp.rows_per_group;
+  sp.S = S;
+  sp.KVH = pp.KVH;
+  sp.max_ctx = pp.max_ctx;
+  sp.max_pages = pp.max_pages;
+  sp.cap = pp.item_cap;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (va::launch_schedule(sp, s) != hipSuccess) return VA_EHIP;
   if (va::launch_partial(pp, plan->prob.kv_dtype, plan->tiling.nt, s) != hipSuccess) return VA_EHIP;
   if (S > 1 && va::launch_merge(merge_params(pp, out, lse), s) != hipSuccess) return VA_EHIP;
   return VA_OK;

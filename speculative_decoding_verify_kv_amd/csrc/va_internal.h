@@ -23,6 +23,12 @@ constexpr size_t kScratchBytes = (size_t)64 << 20;
 // sequence's rows some parallelism but save each split's fixed cost (Q
 // staging, partial write-back, a workgroup slot) and its partials.
 constexpr int kMinSplitPages = 32;
+// Ragged plans: most sequences one call may hold (the work-list pass keeps
+// a few words per sequence in LDS).
+constexpr int kMaxSchedSeqs = 2048;
+// Ragged calls: rows whose sequence has at most this many splits are merged
+// one wave per (row, head) rather than one workgroup.
+constexpr int kMergeLightSplits = 8;
 
 // Kernel-side dtype codes (same values as va_dtype).
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kQ8 = 3 };
@@ -44,6 +50,8 @@ struct PartialParams {
   float* part_m;          // [S][nrows]  (log2 units)
   float* part_l;          // [S][nrows]
   int32_t* part_n;        // ragged calls: [nrows] splits that hold keys of the row's sequence (written by split 0); else NULL
+  const int2* items;      // ragged calls: the work list (sequence, row group << 16 | split << 8 | KV head)
+  const int32_t* item_count;  // ragged calls: entries of `items` in use
   uint32_t* flags;
   int32_t num_seqs, B, H, KVH, G, D;  // B: rows per sequence (ragged: the largest count)
   int32_t total_rows;     // ragged: capacity of the packed rows
@@ -55,6 +63,7 @@ struct PartialParams {
   int32_t direct;         // 1: write out/lse, 0: write partials
   float scale_log2;       // softmax scale * log2(e)
   int64_t nrows;          // num_seqs * B * H
+  int32_t item_cap;       // ragged calls: workgroups launched (entries `items` can hold)
 };
 
 struct MergeParams {
@@ -64,7 +73,8 @@ struct MergeParams {
   const int32_t* part_n;
   void* out;
   float* lse;
-  const int32_t* live_rows; // ragged: &cu_rows[num_seqs]; rows from live_rows[0] * heads on are skipped
+  const int32_t* merge_rows;  // ragged: packed rows to merge, in order; NULL: row = block / heads
+  const int32_t* merge_count; // ragged: [0] entries of merge_rows in use, [1] the leading ones merged by workgroup
   int32_t heads;
   int32_t S, D, out_dtype;
   int64_t nrows;
@@ -105,6 +115,18 @@ struct PromoteParams {
   int32_t esz, kv_is_q8;
 };
 
+// The work-list pass of a ragged call (one workgroup, ahead of the partial
+// kernel): the partial kernel's items and the merge's row order.
+struct ScheduleParams {
+  const int32_t* cu_rows;
+  const int32_t* ctx_lens;
+  int32_t* count;         // [0] items listed, [1] rows listed, [2] of them with more than kMergeLightSplits splits
+  int2* items;            // [cap]
+  int32_t* merge_rows;    // [total_rows]
+  uint32_t* flags;
+  int32_t num_seqs, B, total_rows, G, qrows, S, KVH, max_ctx, max_pages, cap;
+};
+
 // Tiling the plan picks for the partial kernel.
 struct Tiling {
   int nt;          // 16-row MFMA tiles per workgroup (2, 4 or 6)
@@ -116,6 +138,7 @@ bool partial_supported(int D, int kv_dtype, int nt);
 
 hipError_t launch_partial(const PartialParams& p, int kv_dtype, int nt, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_schedule(const ScheduleParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 size_t promote_row_bytes(int D, int kv_dtype);
 hipError_t launch_promote(const PromoteParams& p, hipStream_t stream);

@@ -55,14 +55,127 @@ template <> struct VecT<1> { typedef float type; };
 constexpr int kMergeWaves = 8;
 constexpr int kMergeBatch = 4;   // split rows in flight per wave
 
+template <int E>
+__device__ __forceinline__ void store_row(const MergeParams& p, int64_t R, int lane, const float* sum, float inv,
+                                          bool nan_row, float M, float L) {
+  constexpr int D = 64 * E;
+  const int64_t o = R * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float x = sum[e] * inv;
+    if (p.out_dtype == kF32) reinterpret_cast<float*>(p.out)[o + e] = x;
+    else if (p.out_dtype == kF16) reinterpret_cast<h16*>(p.out)[o + e] = (h16)x;
+    else reinterpret_cast<uint16_t*>(p.out)[o + e] = (uint16_t)f32_to_bf16_bits(x);
+  }
+  if (lane == 0 && p.lse)
+    p.lse[R] = nan_row ? __builtin_nanf("") : 0.6931471805599453f * (M + __builtin_log2f(L));
+}
+
+// One wave merges (row, head) R alone: for ragged rows whose sequence has at
+// most kMergeLightSplits splits.  Same arithmetic, in the same order, as the
+// workgroup form below gives such a row (each of its waves then holds at
+// most one split, and their sums are added in wave order), so the two agree
+// bit for bit.
+template <int D>
+__device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, int lane) {
+  constexpr int E = D / 64;
+  constexpr int HJ = kMaxSplits / 64;
+  typedef typename VecT<E>::type vec;
+  const int S = p.S;
+  const int Sr = max(1, min(S, *reinterpret_cast<const __attribute__((address_space(4))) int*>(
+                                    (uintptr_t)(p.part_n + R))));
+  const float* base = p.part_o + R * D + E * lane;
+  const int64_t kstride = p.nrows * D;
+  float mh[HJ], lh[HJ];
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    const int k = lane + 64 * j;
+    mh[j] = -INFINITY;
+    lh[j] = 0.f;
+    if (k < Sr) {
+      mh[j] = p.part_m[(int64_t)k * p.nrows + R];
+      lh[j] = p.part_l[(int64_t)k * p.nrows + R];
+    }
+  }
+  float M = -INFINITY;
+  bool nan_row = false;
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    nan_row |= (lh[j] != lh[j]);
+    if (lh[j] > 0.f) M = fmaxf(M, mh[j]);
+  }
+  M = wave_max(M);
+  nan_row = __builtin_amdgcn_ballot_w64(nan_row) != 0;
+  float wk[HJ];
+  float Lpart = 0.f;
+#pragma unroll
+  for (int j = 0; j < HJ; ++j) {
+    wk[j] = (lh[j] > 0.f) ? __builtin_amdgcn_exp2f(mh[j] - M) : 0.f;
+    Lpart = __builtin_fmaf(wk[j], lh[j], Lpart);
+  }
+  const float L = wave_sum(Lpart);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < Sr; k0 += kMergeBatch) {
+    vec v[kMergeBatch];
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b)
+      v[b] = *reinterpret_cast<const vec*>(base + (int64_t)min(k0 + b, S - 1) * kstride);
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int k = k0 + b;  // wave-uniform
+      const int j = k >> 6;
+      float wsel = wk[0];
+#pragma unroll
+      for (int jj = 1; jj < HJ; ++jj) wsel = (j == jj) ? wk[jj] : wsel;
+      const float w = (k < Sr) ? __shfl(wsel, k & 63) : 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float x;
+        if constexpr (E == 1) x = v[b];
+        else x = v[b][e];
+        // the workgroup form: this split's wave sum (the rounded product, a
+        // negative zero made positive), added to the running sum in order
+        const float t = ((w > 0.f) ? __fmul_rn(w, x) : 0.f) + 0.f;
+        if (k < Sr) acc[e] += t;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] += 0.f;
+  const float inv = nan_row ? __builtin_nanf("") : 1.0f / L;
+  store_row<E>(p, R, lane, acc, inv, nan_row, M, L);
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const MergeParams p) {
   constexpr int E = D / 64;  // outputs per lane
   constexpr int HJ = kMaxSplits / 64;
   typedef typename VecT<E>::type vec;
   __shared__ float red[kMergeWaves][D];
-  const int64_t R = blockIdx.x;
-  if (p.live_rows && R >= (int64_t)p.live_rows[0] * p.heads) return;  // past the packed rows in use
+  // (row, head) of this workgroup: block / heads and block % heads, or in a
+  // ragged call the row at that place of the work list's row order (rows
+  // with the most splits first; blocks past the rows in use leave)
+  // Ragged calls: the rows with more than kMergeLightSplits splits lead the
+  // list, one workgroup per (row, head); the rest follow, one wave per
+  // (row, head), 8 to a workgroup.
+  int64_t R = blockIdx.x;
+  if (p.merge_rows) {
+    const auto* mc = reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)p.merge_count);
+    const int64_t heavy = (int64_t)mc[1] * p.heads;
+    if (R >= heavy) {
+      const int64_t pr = heavy + (R - heavy) * kMergeWaves + (threadIdx.x >> 6);
+      if (pr >= (int64_t)mc[0] * p.heads) return;
+      const int64_t k = pr / p.heads;
+      const int row = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.merge_rows + k));
+      merge_one_wave<D>(p, (int64_t)row * p.heads + (pr - k * p.heads), threadIdx.x & 63);
+      return;
+    }
+    const int64_t k = R / p.heads;
+    const int row = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.merge_rows + k));
+    R = (int64_t)row * p.heads + (R - k * p.heads);
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = p.S;
@@ -114,7 +227,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
 #pragma unroll
     for (int j = 0; j < HJ; ++j) {
       const float wk = (lh[j] > 0.f) ? __builtin_amdgcn_exp2f(mh[j] - M) : 0.f;
-      Lpart += wk * lh[j];
+      Lpart = __builtin_fmaf(wk, lh[j], Lpart);
       wsh[lane + 64 * j] = wk;
     }
     L = wave_sum(Lpart);
@@ -148,19 +261,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   if (wave != 0) return;
 
   const float inv = nan_row ? __builtin_nanf("") : 1.0f / L;
-  const int64_t o = R * D + E * lane;
+  float sum[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    float sum = 0.f;
+    sum[e] = 0.f;
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) sum += red[w][E * lane + e];
-    const float x = sum * inv;
-    if (p.out_dtype == kF32) reinterpret_cast<float*>(p.out)[o + e] = x;
-    else if (p.out_dtype == kF16) reinterpret_cast<h16*>(p.out)[o + e] = (h16)x;
-    else reinterpret_cast<uint16_t*>(p.out)[o + e] = (uint16_t)f32_to_bf16_bits(x);
+    for (int w = 0; w < kMergeWaves; ++w) sum[e] += red[w][E * lane + e];
   }
-  if (lane == 0 && p.lse)
-    p.lse[R] = nan_row ? __builtin_nanf("") : 0.6931471805599453f * (M + __builtin_log2f(L));
+  store_row<E>(p, R, lane, sum, inv, nan_row, M, L);
 }
 
 }  // namespace

@@ -300,51 +300,24 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   // Workgroup -> (split, row group).  When every split has several row
   // groups, the row groups of one split get block ids 8 apart: blocks are
   // dealt round-robin to the 8 XCDs, so they share one L2 and run together.
-  // Ragged calls (SQ) take the grid as (split counted down, row group, KV
-  // head).  The row groups of all sequences are numbered in sequence order
-  // (sequence s has ceil(rows_s * G / QROWS) of them), so no workgroup is
-  // spent on a group a sequence does not have; each wave finds its sequence
-  // with a prefix sum of those counts over cu_rows, 64 sequences at a time.
-  // The splits of one (row group, KV head) have consecutive block ids, and
-  // blocks are dealt round-robin to the 8 XCDs, so a long sequence's splits
-  // spread over all of them: with the row group fastest, four one-group
-  // sequences over 4 KV heads put every split of a sequence on two XCDs
-  // (the paged four-sequence batch ran 141 us that way, 78 us this way).
+  // Ragged calls (SQ) take their (sequence, row group, split, KV head) from
+  // the work list the schedule pass wrote: entry blockIdx.x, while entries
+  // are in use (the grid holds as many workgroups as the list can).  The list
+  // is dense and longest first, so the workgroups that do work are dealt
+  // evenly to the 8 XCDs (round-robin by block id) and the long ones start
+  // first; the pass also reports bad cu_rows entries (their sequences have
+  // no entries).
   int s, kvh, split, rg;
   if constexpr (SQ) {
-    split = p.S - 1 - (int)blockIdx.x;
-    const int g = blockIdx.y;
-    kvh = blockIdx.z;
-    s = -1;
-    rg = 0;
-    int before = 0;
-    bool any_bad = false;
-    for (int base = 0; base < p.num_seqs; base += 64) {
-      const int si = base + lane;
-      int cnt = 0;
-      bool bad = false;
-      if (si < p.num_seqs) {
-        const int a = p.cu_rows[si], e = p.cu_rows[si + 1];
-        bad = a < 0 || e < a || e > p.total_rows || e - a > p.B;
-        cnt = bad ? 0 : ((e - a) * p.G + QROWS - 1) / QROWS;
-      }
-      any_bad |= __ballot(bad) != 0;
-      int inc = cnt;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(inc, o);
-        if (lane >= o) inc += t;
-      }
-      const uint64_t hit = __ballot(before + inc > g);
-      if (hit && s < 0) {
-        const int l = __builtin_ctzll(hit);
-        s = base + l;
-        rg = g - before - (__builtin_amdgcn_readlane(inc, l) - __builtin_amdgcn_readlane(cnt, l));
-      }
-      before += __builtin_amdgcn_readlane(inc, 63);
-    }
-    if (any_bad && tid == 0 && g == 0 && kvh == 0 && split == 0) atomicOr(p.flags, (uint32_t)VA_FLAG_BAD_ROWS);
-    if (s < 0) return;  // past the last sequence's groups
+    const auto* cnt = reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)p.item_count);
+    if ((int)blockIdx.x >= cnt[0]) return;
+    const auto* it =
+        reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.items + blockIdx.x));
+    s = it[0];
+    const int packed = it[1];
+    rg = packed >> 16;
+    split = (packed >> 8) & 255;
+    kvh = packed & 255;
   } else {
     s = blockIdx.z;
     kvh = blockIdx.y;
@@ -1182,15 +1155,9 @@ bool partial_supported(int D, int kv_dtype, int nt) {
 template <int D, int KVT, int NT>
 static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
   dim3 grid((unsigned)(p.S * p.row_groups), (unsigned)p.KVH, (unsigned)p.num_seqs);
-  if (p.part_n) {
-    // Row groups over all sequences: sum_s ceil(rows_s * G / QROWS) with
-    // sum_s rows_s <= total_rows while cu_rows is valid up to s.
-    constexpr int64_t QR = 16 * NT;
-    const int64_t all = (int64_t)p.num_seqs * p.row_groups;
-    const int64_t bound = ((int64_t)p.total_rows * p.G + (int64_t)p.num_seqs * (QR - 1)) / QR;
-    const int64_t groups = bound < all ? (bound > 1 ? bound : 1) : all;
-    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>),
-                       dim3((unsigned)p.S, (unsigned)groups, (unsigned)p.KVH),
+  if (p.items) {
+    // ragged: one workgroup per entry the work list can hold
+    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>), dim3((unsigned)p.item_cap),
                        dim3(kBlockThreads), 0, stream, p);
   }
   else

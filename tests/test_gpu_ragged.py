@@ -106,16 +106,19 @@ def test_long_prefill_segment(S_):
     check_parity(got[:w.total_rows], ref, "f16", f"prefill300 S={S_}")
 
 
-@pytest.mark.parametrize("S_", [1, 8])
-def test_uniform_rows_through_ragged_entry_bitwise(S_):
+@pytest.mark.parametrize("S_,ctxs", [(1, (4096, 4112, 5000, 6000)), (8, (4096, 4112, 5000, 6000)),
+                                     (16, (8192, 8200, 12000, 16000))])
+def test_uniform_rows_through_ragged_entry_bitwise(S_, ctxs):
     # B rows per sequence written as cu_rows = [0, B, 2B, ...]: the same plan
     # shape and split count must give the same bits as verify_attn_run.  The
-    # contexts are long enough (>= 8 splits of 32 pages) that the ragged rule
+    # contexts are long enough (>= S splits of 32 pages) that the ragged rule
     # (a sequence's splits hold at least 32 pages) cuts the same splits as
     # the uniform one; shorter sequences take fewer, longer splits there.
+    # At S = 8 the ragged merge takes each row with one wave (at most 8
+    # splits), at S = 16 with a workgroup, as the uniform merge always does.
     import torch
 
-    w = S.paged_ragged(ctxs=(4096, 4112, 5000, 6000))
+    w = S.paged_ragged(ctxs=ctxs)
     wr = copy.deepcopy(w)
     wr.cu_rows = np.arange(0, w.num_seqs * w.B + 1, w.B, dtype=np.int32)
     say(f"[case] uniform via ragged S={S_}")
@@ -280,9 +283,8 @@ def test_short_sequences_leave_their_extra_splits(S_):
 
 @pytest.mark.parametrize("kv,S_", [("q8_0", 0), ("f16", 3)])
 def test_many_sequences(kv, S_):
-    # 150 sequences of 0-4 rows: the kernel numbers row groups over all
-    # sequences with a prefix sum taken 64 sequences at a time, so this spans
-    # three such passes, with empty sequences at and around their edges
+    # 150 sequences of 0-4 rows, empty ones among them: the work list orders
+    # them by size and numbers their row groups with a block-wide prefix sum
     rng = np.random.default_rng(29)
     rows = rng.integers(0, 5, 150)
     rows[[0, 63, 64, 127, 128, 149]] = [0, 0, 3, 0, 2, 0]
@@ -295,3 +297,91 @@ def test_many_sequences(kv, S_):
     assert flags == 0
     check_parity(got[:n], ref, "f16", f"150 sequences kv={kv} S={plan.info().num_splits if S_ == 0 else S_}")
     assert np.abs(lse[:n] - lref).max() <= 2e-3
+
+
+def _work_list_model(w, cu, S, plan):
+    """The work list a ragged call should hold, written out from its rule: each
+    sequence's row groups (ceil(rows * G / rows_per_group)), pages per split
+    (at least 32) and splits from its own context; sequences ordered by pages
+    per split, then split count, descending (ties by index); each sequence's
+    entries by split, row group, KV head; then its packed rows for the merge."""
+    info = plan.info()
+    G = w.H // w.KVH
+    seqs = []
+    for s in range(w.num_seqs):
+        a, e = int(cu[s]), int(cu[s + 1])
+        rows = e - a
+        groups = -(-rows * G // info.rows_per_group)
+        ctx = int(w.ctx_lens[s])
+        np_ = -(-ctx // 16)
+        pp = max(-(-np_ // S), 32)
+        splits = max(1, -(-np_ // pp))
+        items = groups * splits * w.KVH
+        key = pp * 512 + splits if items else 0
+        seqs.append((key, s, a, rows, groups, splits, items))
+    order = sorted(seqs, key=lambda t: (-t[0], t[1]))
+    items, merge_rows = [], []
+    for key, s, a, rows, groups, splits, n in order:
+        for sp in range(splits):
+            for g in range(groups):
+                for kvh in range(w.KVH):
+                    items.append((s, (g << 16) | (sp << 8) | kvh))
+        merge_rows.extend(range(a, a + rows))
+    return items, merge_rows
+
+
+def _read_work_list(ws, w, plan):
+    info = plan.info()
+    nrows = plan.problem.max_total_rows * w.H
+    smax = info.max_splits
+    off = 256
+    if smax > 1:
+        off = -(-(256 + smax * nrows * (w.D + 2) * 4 + nrows * 4) // 256) * 256
+    raw = ws.cpu().numpy()
+    cnt = raw[off:off + 8].view(np.int32)
+    mr_bytes = -(-plan.problem.max_total_rows * 4 // 16) * 16
+    mrows = raw[off + 16:off + 16 + 4 * int(cnt[1])].view(np.int32)
+    it = raw[off + 16 + mr_bytes:off + 16 + mr_bytes + 8 * int(cnt[0])].view(np.int32).reshape(-1, 2)
+    return int(cnt[0]), int(cnt[1]), it, mrows
+
+
+@pytest.mark.parametrize("name", ["mixed", "paged4", "many"])
+def test_work_list_matches_its_rule(name):
+    """The schedule pass's work list, read back from the workspace, equals the
+    list its rule gives, entry for entry (integer work: bit-exact)."""
+    import torch
+
+    if name == "mixed":
+        w = S.mixed_lowering()
+        cu = w.cu_rows
+    elif name == "paged4":
+        w = copy.deepcopy(S.paged_ragged())
+        w.parent = None
+        cu = np.arange(0, 65, 16, dtype=np.int32)
+        w.cu_rows = cu
+    else:
+        rng = np.random.default_rng(41)
+        counts = rng.integers(0, 5, size=150)
+        ctxs = rng.integers(8, 3000, size=150)
+        w = S.make_workload("sched_many", ctx_lens=list(ctxs), rows=list(counts), H=8, KVH=2, D=64,
+                            q_dtype="bf16", kv_dtype="q8_0", seed=41, permute=True)
+        cu = w.cu_rows
+    say(f"[case] work list {name}")
+    dev = vdev.to_device(w)
+    for S_ in (0, 8):
+        plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f16"), S_, 0)
+        Sc = S_ or plan.info().num_splits
+        ws = vdev.workspace(plan)
+        cap = plan.problem.max_total_rows
+        out = torch.empty((cap, w.H, w.D), dtype=torch.float16, device="cuda")
+        lse = torch.empty((cap, w.H), dtype=torch.float32, device="cuda")
+        cu_d = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+        va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                                  dev["block_table"], dev["ctx_lens"], cu_d, dev["parent"], S_, out, lse, ws)
+        torch.cuda.synchronize()
+        n_items, n_rows, it, mrows = _read_work_list(ws, w, plan)
+        want_items, want_rows = _work_list_model(w, cu, Sc, plan)
+        say(f"  S={Sc}: {n_items} entries, {n_rows} rows")
+        assert n_items == len(want_items) and n_rows == len(want_rows)
+        assert [tuple(x) for x in it.tolist()] == want_items
+        assert mrows.tolist() == want_rows

@@ -282,16 +282,34 @@ def test_ragged_plan_sizes_by_packed_rows(lib):
     plan = va.verify_attn_plan_for_cus(prob, 8, 256)
     info = plan.info()
     assert info.rows_per_group == 96 and info.row_groups == 7  # 600 rows -> 38 tiles -> 7 groups of 6
-    assert info.workspace_bytes == 256 + 8 * 149 * 24 * 258 * 4 + 149 * 24 * 4
+    # header, fp32 partials of 8 splits and one int32 per (row, head), then
+    # (256-byte aligned) the work list: 2 counts in 16 bytes, the 149 packed
+    # rows (padded to 16 bytes) and 8 splits x 14 row groups x 4 KV heads
+    # entries of 8 bytes (14 = (149 * 6 + 5 * 95) // 96 groups at most)
+    parts = 256 + 8 * 149 * 24 * 258 * 4 + 149 * 24 * 4
+    assert info.workspace_bytes == -(-parts // 256) * 256 + 16 + 608 + 8 * 14 * 4 * 8
     # the plan's own split count is sized for one long decode sequence (one
-    # row group per KV head) filling the CUs: 2,500 pages in 63 splits of 10
-    # tiles; the shorter sequences of the call keep to fewer splits themselves
+    # row group per KV head) filling the CUs that two minimum-size splits per
+    # KV head of each of the 4 other sequences leave (256 - 32 = 224, 56 per
+    # KV head): 2,500 pages in 53 splits of 12 tiles; the shorter sequences of
+    # the call keep to fewer splits themselves
     info = va.verify_attn_plan_for_cus(prob, 0, 256).info()
-    assert info.num_splits == 63 and info.pages_per_split == 40
+    assert info.num_splits == 53 and info.pages_per_split == 48
+    # one sequence keeps every CU; many keep at least half of them
+    one = qwen(num_seqs=1, rows_per_seq=100, max_total_rows=100, max_ctx=40000, max_pages_per_seq=2500,
+               num_pages=8192)
+    assert va.verify_attn_plan_for_cus(one, 0, 256).info().num_splits == 63
+    many = qwen(num_seqs=40, rows_per_seq=4, max_total_rows=160, max_ctx=40000, max_pages_per_seq=2500,
+                num_pages=8192)
+    assert va.verify_attn_plan_for_cus(many, 0, 256).info().num_splits == 32  # 128 CUs: 32 per KV head, 20 tiles
     # long prefill segments are allowed only in ragged plans
     assert plan_status(qwen(rows_per_seq=65)) == va.VA_EUNSUPPORTED
     assert plan_status(qwen(rows_per_seq=4096, max_total_rows=4096, max_ctx=32768)) == va.VA_OK
     assert plan_status(qwen(rows_per_seq=4097, max_total_rows=4097, max_ctx=32768)) == va.VA_EUNSUPPORTED
+    # the work list holds at most 2,048 sequences and 256 KV heads
+    assert plan_status(qwen(num_seqs=2048, rows_per_seq=1, max_total_rows=2048)) == va.VA_OK
+    assert plan_status(qwen(num_seqs=2049, rows_per_seq=1, max_total_rows=2049)) == va.VA_EUNSUPPORTED
+    assert plan_status(qwen(num_seqs=2049, rows_per_seq=1)) == va.VA_OK  # uniform plans have no such list
     # capacity above num_seqs * rows_per_seq, or negative
     assert plan_status(qwen(num_seqs=2, rows_per_seq=10, max_total_rows=21)) == va.VA_EINVAL
     assert plan_status(qwen(max_total_rows=-1)) == va.VA_EINVAL
