@@ -10,7 +10,10 @@ already resident in HBM.  Eight distinct KV pools (8 x 71 MB, well beyond the
 With --configs it instead times the other workload shapes (fp16 KV at 8K,
 8-bit KV at 8K / 20,676 / 32,768, the paged four-sequence batch, the draft
 tree and the chain sweep B = 4, 8, 16, 32), one JSON line each, with the
-same cold-pool rotation; the default run prints only the headline line.
+same cold-pool rotation, then the steps around the call (KV append and
+quantisation, graph replay, accepted-path promotion) and the ragged calls
+(the paged batch through the ragged entry, the mixed call); the default run
+prints only the headline line.
 
 Prints one JSON line.  value = KV bytes of the valid tokens / time per call
 (GB/s) over the K timed calls, after ~50 ms of untimed calls (the device
@@ -138,13 +141,31 @@ def config_list(S):
         ("8-bit KV, ctx 8192", lambda: S.q8_long(ctx=8192), (0, 8)),
         ("8-bit KV, ctx 20676", lambda: S.q8_long(ctx=20676), (0, 8)),
         ("8-bit KV, ctx 32768", lambda: S.q8_long(ctx=32768), (0, 8)),
-        ("paged 4 x B 16, ctx 1016/1024/1032/40000", lambda: S.paged_ragged(), (0, 8)),
+        ("paged 4 x B 16, ctx 1016/1024/1032/40000", lambda: S.paged_ragged(), (0, 8, 32)),
         ("tree 2 direct + 8 tree rows, ctx 20676", lambda: S.tree_mixed(), (0,)),
         ("chain B 4, ctx 20676", lambda: S.chain(4), (0,)),
         ("chain B 8, ctx 20676", lambda: S.chain(8), (0,)),
         ("chain B 16, ctx 20676", lambda: S.chain(16), (0,)),
         ("chain B 32, ctx 20676", lambda: S.chain(32), (0,)),
     ]
+
+
+def grouped_us(torch, stream, fn, n, group=10):
+    """Per-call time of n calls of fn(i) in groups of `group` back-to-back
+    calls, an event between groups: (mean, median, 95th percentile) in us."""
+    import numpy as np
+
+    ngroups = max(1, n // group)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(ngroups + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for g in range(ngroups):
+        for j in range(group):
+            fn(g * group + j)
+        evs[g + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([1e3 * evs[g].elapsed_time(evs[g + 1]) / group for g in range(ngroups)])
+    return float(per.mean()), float(np.median(per)), float(np.percentile(per, 95))
 
 
 def time_configs(args, torch, va, vdev, S):
@@ -185,10 +206,12 @@ def time_configs(args, torch, va, vdev, S):
             b.record(stream)
             torch.cuda.synchronize()
             us = 1e3 * a.elapsed_time(b) / args.steps
+            _, med, p95 = grouped_us(torch, stream, call, args.steps)
             info = plan.info()
             gbps = kv_bytes / (us * 1e-6) / 1e9
             print(json.dumps({"config": label, "workload": w.name, "splits": info.num_splits,
                               "row_groups": info.row_groups, "us_per_call": round(us, 2),
+                              "us_per_call_median": round(med, 2), "us_per_call_p95": round(p95, 2),
                               "kv_bytes_per_call": kv_bytes, "GBps": round(gbps, 1),
                               "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "kv_pools_rotated": npools,
                               "flags": va.verify_attn_read_flags(plan, ws, stream)}), flush=True)
@@ -212,6 +235,8 @@ def time_next_rows(args, torch, va, vdev, S):
 
     stream = torch.cuda.current_stream()
 
+    last = {}
+
     def timed(fn, n):
         for i in range(min(n, 200)):
             fn(i)
@@ -223,10 +248,13 @@ def time_next_rows(args, torch, va, vdev, S):
             fn(i)
         b.record(stream)
         torch.cuda.synchronize()
+        _, last["median"], last["p95"] = grouped_us(torch, stream, fn, n)
         return 1e3 * a.elapsed_time(b) / n
 
     def emit(label, w, us, extra):
-        print(json.dumps({"config": label, "workload": w.name, "us_per_call": round(us, 2), **extra}), flush=True)
+        print(json.dumps({"config": label, "workload": w.name, "us_per_call": round(us, 2),
+                          "us_per_call_median": round(last["median"], 2), "us_per_call_p95": round(last["p95"], 2),
+                          **extra}), flush=True)
 
     # KV append + quantise of the 16 drafted rows (bf16 in, 8-bit pool)
     w = S.q8_long(ctx=32768)
@@ -266,6 +294,8 @@ def time_next_rows(args, torch, va, vdev, S):
                 call(i, cs)
     stream.wait_stream(side)
     replay = timed(lambda i: g.replay(), max(1, args.steps // npools)) / npools
+    last["median"] /= npools  # per call, as `replay`
+    last["p95"] /= npools
     kv = w.kv_bytes_valid()
     emit("headline call replayed from a captured graph (8 calls per graph)", w, replay,
          {"eager_us_per_call": round(eager, 2), "GBps": round(kv / (replay * 1e-6) / 1e9, 1),
