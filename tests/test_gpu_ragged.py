@@ -282,13 +282,17 @@ def test_short_sequences_leave_their_extra_splits(S_):
 
 
 @pytest.mark.parametrize("kv,S_", [("q8_0", 0), ("f16", 3)])
-def test_many_sequences(kv, S_):
-    # 150 sequences of 0-4 rows, empty ones among them: the work list orders
-    # them by size and numbers their row groups with a block-wide prefix sum
+@pytest.mark.parametrize("nseq", [150, 64, 65])
+def test_many_sequences(kv, S_, nseq):
+    # 150 (and 64, 65) sequences of 0-4 rows, empty ones among them: the work
+    # list orders them by size and numbers their row groups (up to 64
+    # sequences by the one-wave pass, a lane each; 65 and more by the
+    # one-workgroup pass)
     rng = np.random.default_rng(29)
     rows = rng.integers(0, 5, 150)
     rows[[0, 63, 64, 127, 128, 149]] = [0, 0, 3, 0, 2, 0]
     ctxs = rows + rng.integers(1, 150, 150)
+    rows, ctxs = rows[:nseq], ctxs[:nseq]
     w = tiny_ragged(kv, seed=29, rows=tuple(int(r) for r in rows), ctxs=tuple(int(c) for c in ctxs), tree=False)
     say(f"[case] {len(rows)} ragged sequences, {int(rows.sum())} rows, kv={kv} S={S_}")
     ref, lref = oracle.attention(w)
@@ -320,14 +324,15 @@ def _work_list_model(w, cu, S, plan):
         key = pp * 512 + splits if items else 0
         seqs.append((key, s, a, rows, groups, splits, items))
     order = sorted(seqs, key=lambda t: (-t[0], t[1]))
-    items, merge_rows = [], []
+    items, merge_rows, heavy = [], [], 0
     for key, s, a, rows, groups, splits, n in order:
         for sp in range(splits):
             for g in range(groups):
                 for kvh in range(w.KVH):
                     items.append((s, (g << 16) | (sp << 8) | kvh))
         merge_rows.extend(range(a, a + rows))
-    return items, merge_rows
+        heavy += rows if splits > 8 else 0
+    return items, merge_rows, heavy
 
 
 def _read_work_list(ws, w, plan):
@@ -338,17 +343,19 @@ def _read_work_list(ws, w, plan):
     if smax > 1:
         off = -(-(256 + smax * nrows * (w.D + 2) * 4 + nrows * 4) // 256) * 256
     raw = ws.cpu().numpy()
-    cnt = raw[off:off + 8].view(np.int32)
+    cnt = raw[off:off + 12].view(np.int32)
     mr_bytes = -(-plan.problem.max_total_rows * 4 // 16) * 16
     mrows = raw[off + 16:off + 16 + 4 * int(cnt[1])].view(np.int32)
     it = raw[off + 16 + mr_bytes:off + 16 + mr_bytes + 8 * int(cnt[0])].view(np.int32).reshape(-1, 2)
-    return int(cnt[0]), int(cnt[1]), it, mrows
+    return int(cnt[0]), int(cnt[1]), int(cnt[2]), it, mrows
 
 
 @pytest.mark.parametrize("name", ["mixed", "paged4", "many"])
 def test_work_list_matches_its_rule(name):
-    """The schedule pass's work list, read back from the workspace, equals the
-    list its rule gives, entry for entry (integer work: bit-exact)."""
+    """The work list, read back from the workspace, equals the list its rule
+    gives, entry for entry (integer work: bit-exact): the counts, the
+    entries and the merge's row order, from the one-wave pass (up to 64
+    sequences) and from the one-workgroup pass (150 sequences)."""
     import torch
 
     if name == "mixed":
@@ -379,9 +386,9 @@ def test_work_list_matches_its_rule(name):
         va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
                                   dev["block_table"], dev["ctx_lens"], cu_d, dev["parent"], S_, out, lse, ws)
         torch.cuda.synchronize()
-        n_items, n_rows, it, mrows = _read_work_list(ws, w, plan)
-        want_items, want_rows = _work_list_model(w, cu, Sc, plan)
-        say(f"  S={Sc}: {n_items} entries, {n_rows} rows")
-        assert n_items == len(want_items) and n_rows == len(want_rows)
-        assert [tuple(x) for x in it.tolist()] == want_items
+        n_items, n_rows, n_heavy, it, mrows = _read_work_list(ws, w, plan)
+        want_items, want_rows, want_heavy = _work_list_model(w, cu, Sc, plan)
+        say(f"  S={Sc}: {n_items} entries, {n_rows} rows, {n_heavy} merged by workgroup")
+        assert n_items == len(want_items) and n_rows == len(want_rows) and n_heavy == want_heavy
         assert mrows.tolist() == want_rows
+        assert [tuple(x) for x in it.tolist()] == want_items
