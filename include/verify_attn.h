@@ -256,7 +256,11 @@ va_status verify_attn_run_noalloc(const va_plan* plan, const void* q, const void
  * longest work first, packed densely so the workgroups spread evenly over
  * the device), the partial kernel over that list, and the merge.  A plan
  * with num_splits = 0 sizes S for one sequence at max_ctx plus num_seqs - 1
- * sequences of up to 64 pages running as one wave of workgroups.
+ * sequences of up to 64 pages running as one wave of workgroups; batches of
+ * B rows per sequence whose contexts differ widely (a long decode beside
+ * short ones) therefore run faster here with cu_rows = [0, B, 2B, ...] than
+ * through verify_attn_run, whose plan sizes S for every sequence at max_ctx
+ * (and suits batches of similar contexts better).
  * Limits: num_seqs <= 2048 and num_kv_heads <= 256 (VA_EUNSUPPORTED).
  * A bad cu_rows entry sets VA_FLAG_BAD_ROWS; that sequence writes nothing
  * (outputs of rows it would own are unspecified).  Sequences are taken in
