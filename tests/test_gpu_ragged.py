@@ -303,29 +303,60 @@ def test_many_sequences(kv, S_, nseq):
     assert np.abs(lse[:n] - lref).max() <= 2e-3
 
 
-def _work_list_model(w, cu, S, plan):
-    """The work list a ragged call should hold, written out from its rule: each
-    sequence's row groups (ceil(rows * G / rows_per_group)), pages per split
-    (at least 32) and splits from its own context; sequences ordered by pages
-    per split, then split count, descending (ties by index); each sequence's
-    entries by split, row group, KV head; then its packed rows for the merge."""
+def _item_cap(w, plan, S):
+    """Entries the grid holds: S * groups * KVH, groups bounding the row groups
+    of sequences whose rows fill the packed capacity."""
     info = plan.info()
     G = w.H // w.KVH
+    qr = info.rows_per_group
+    cap_rows = plan.problem.max_total_rows
+    bound = (cap_rows * G + w.num_seqs * (qr - 1)) // qr
+    groups = max(1, min(bound, w.num_seqs * info.row_groups))
+    return S * groups * w.KVH
+
+
+def _work_list_model(w, cu, S, plan, ctx_lens=None):
+    """The work list a ragged call should hold, written out from its rule: each
+    sequence's row groups (ceil(rows * G / rows_per_group); none for a bad
+    cu_rows entry), pages per split (at least 32) and splits from its own
+    context (one split for a bad context); sequences taken in index order
+    while their rows fit the packed capacity and their entries the grid;
+    those ordered by split count, then pages per split, descending (ties by
+    index); each sequence's entries by split, row group, KV head; then its
+    packed rows for the merge, and how many of those rows have more than 8
+    splits."""
+    info = plan.info()
+    G = w.H // w.KVH
+    cap_rows = plan.problem.max_total_rows
+    B = plan.problem.rows_per_seq
+    max_ctx = plan.problem.max_ctx
+    max_pages = plan.problem.max_pages_per_seq
+    cap = _item_cap(w, plan, S)
+    ctx_lens = w.ctx_lens if ctx_lens is None else ctx_lens
     seqs = []
+    ib = rb = 0
     for s in range(w.num_seqs):
         a, e = int(cu[s]), int(cu[s + 1])
-        rows = e - a
+        bad = a < 0 or e < a or e > cap_rows or e - a > B
+        rows = 0 if bad else e - a
         groups = -(-rows * G // info.rows_per_group)
-        ctx = int(w.ctx_lens[s])
-        np_ = -(-ctx // 16)
+        ctx = int(ctx_lens[s])
+        ctx_bad = ctx < rows or ctx > max_ctx or ctx > max_pages * 16
+        np_ = 0 if ctx_bad else -(-ctx // 16)
         pp = max(-(-np_ // S), 32)
         splits = max(1, -(-np_ // pp))
         items = groups * splits * w.KVH
-        key = pp * 512 + splits if items else 0
+        ib += items
+        rb += rows
+        fits = ib <= cap and rb <= cap_rows
+        key = (splits << 21) + min(pp, (1 << 21) - 1) if (fits and items) else 0
         seqs.append((key, s, a, rows, groups, splits, items))
+    seqs = [t if t[0] else (0, t[1], t[2], 0, t[4], t[5], 0) for t in seqs]
     order = sorted(seqs, key=lambda t: (-t[0], t[1]))
     items, merge_rows, heavy = [], [], 0
     for key, s, a, rows, groups, splits, n in order:
+        if not n:  # not taken, or nothing to do
+            continue
         for sp in range(splits):
             for g in range(groups):
                 for kvh in range(w.KVH):
@@ -392,3 +423,50 @@ def test_work_list_matches_its_rule(name):
         assert n_items == len(want_items) and n_rows == len(want_rows) and n_heavy == want_heavy
         assert mrows.tolist() == want_rows
         assert [tuple(x) for x in it.tolist()] == want_items
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_work_list_random_batches(seed):
+    """Random batches (1 to 150 sequences, 0 to 9 rows, contexts up to 3,000,
+    the plan's S or a random one), some with bad cu_rows entries or contexts:
+    the list read back equals its rule, entry for entry, and the bad entries
+    are flagged."""
+    import torch
+
+    rng = np.random.default_rng(900 + seed)
+    n = int(rng.choice([1, 2, 5, 17, 63, 64, 65, 150]))
+    rows = rng.integers(0, 10, n)
+    ctxs = rows + rng.integers(1, 3000, n)
+    w = S.make_workload(f"sched_rand{seed}", ctx_lens=list(ctxs), rows=list(rows), H=8, KVH=2, D=64,
+                        q_dtype="bf16", kv_dtype="q8_0", seed=900 + seed, permute=True)
+    dev = vdev.to_device(w)
+    S_ = int(rng.choice([0, 0, 1, 3, 8, 40]))
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f16"), S_, 0)
+    Sc = S_ or plan.info().num_splits
+    cu = w.cu_rows.copy()
+    ctx_live = w.ctx_lens.copy()
+    if seed % 3 == 1 and n > 2:  # a decreasing entry (its sequence and the next change)
+        k = int(rng.integers(1, n))
+        cu[k] = max(0, int(cu[k - 1]) - 1)
+    cap_rows, B = plan.problem.max_total_rows, plan.problem.rows_per_seq
+    expect_bad_rows = any(cu[s] < 0 or cu[s + 1] < cu[s] or cu[s + 1] > cap_rows or cu[s + 1] - cu[s] > B
+                          for s in range(n))
+    if seed % 3 == 2:  # a context past max_ctx: that sequence keeps one split
+        ctx_live[int(rng.integers(0, n))] = plan.problem.max_ctx + 1
+    say(f"[case] work list random seed={seed} n={n} rows={int(rows.sum())} S={Sc}")
+    ws = vdev.workspace(plan)
+    cap = plan.problem.max_total_rows
+    out = torch.empty((cap, w.H, w.D), dtype=torch.float16, device="cuda")
+    lse = torch.empty((cap, w.H), dtype=torch.float32, device="cuda")
+    cu_d = torch.from_numpy(np.asarray(cu, np.int32)).cuda()
+    ctx_d = torch.from_numpy(np.asarray(ctx_live, np.int32)).cuda()
+    va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                              dev["block_table"], ctx_d, cu_d, None, S_, out, lse, ws)
+    torch.cuda.synchronize()
+    n_items, n_rows, n_heavy, it, mrows = _read_work_list(ws, w, plan)
+    want_items, want_rows, want_heavy = _work_list_model(w, cu, Sc, plan, ctx_live)
+    assert (n_items, n_rows, n_heavy) == (len(want_items), len(want_rows), want_heavy)
+    assert mrows.tolist() == want_rows
+    assert [tuple(x) for x in it.tolist()] == want_items
+    flags = va.verify_attn_read_flags(plan, ws)
+    assert bool(flags & va.VA_FLAG_BAD_ROWS) == expect_bad_rows
