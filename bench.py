@@ -47,24 +47,34 @@ MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 on MI355X
 NPOOLS = 8
 
 
+def build_digest(root, src):
+    """sha256 of a kernel source followed by its own compiler flags (a newline,
+    then the flags joined by spaces): what a counter summary was taken on."""
+    import hashlib
+
+    from speculative_decoding_verify_kv_amd import build as vbuild
+
+    data = open(os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc", src), "rb").read()
+    flags = " ".join(vbuild.PER_SOURCE_FLAGS.get(src, []))
+    return hashlib.sha256(data + b"\n" + flags.encode()).hexdigest()
+
+
 def traffic_from_profile(root):
     """HBM-side bytes per launch of the partial and the merge kernel from the
     committed counter summary: {"partial": B, "merge": B}, or None when either
-    kernel's source changed after the counters were taken."""
-    import hashlib
+    kernel's source or compiler flags changed after the counters were taken."""
     import re
 
     prof = os.path.join(root, "profiles", "verify_partial_q8_b16_h24_kv4_d256_ctx32768_counters.md")
-    csrc = os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc")
     try:
         text = open(prof).read()
-        digests = {k: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
-                   for k, f in (("partial", "verify_partial.hip"), ("merge", "verify_merge.hip"))}
+        digests = {k: build_digest(root, f) for k, f in (("partial", "verify_partial.hip"),
+                                                          ("merge", "verify_merge.hip"))}
     except OSError:
         return None
     out = {}
     for k in ("partial", "merge"):
-        m_sha = re.search(rf"{k}_source_sha256: ([0-9a-f]{{64}})", text)
+        m_sha = re.search(rf"{k}_build_sha256: ([0-9a-f]{{64}})", text)
         m_val = re.search(rf"{k}_traffic_bytes_per_launch: (\d+)", text)
         if not m_sha or not m_val or m_sha.group(1) != digests[k]:
             return None
