@@ -3,27 +3,31 @@
 // A ragged call splits each sequence by its own context (at least
 // kMinSplitPages pages per split), so the (sequence, row group, split, KV
 // head) items of one call differ in size and number from call to call, and
-// only the device knows them (cu_rows and ctx_lens live there).  This
-// one-workgroup kernel runs ahead of the partial kernel and lists the items:
-//   * densely, from item 0: workgroups are dealt to the 8 XCDs round-robin by
-//     block id, so a dense list spreads the work evenly over them, where a
-//     grid holding every possible item would leave the empty ones (which exit
-//     at once) between the real ones and pile more than 32 real workgroups on
-//     some XCDs;
+// only the device knows them (cu_rows and ctx_lens live there).  This pass
+// runs ahead of the partial kernel, as one wave for calls of up to 64
+// sequences and as one workgroup of 1,024 threads for more, and lists:
+//   * the items, densely from item 0: workgroups are dealt to the 8 XCDs
+//     round-robin by block id, so a dense list spreads the work evenly over
+//     them, where a grid holding every possible item would leave the empty
+//     ones (which exit at once) between the real ones and pile more than 32
+//     real workgroups on some XCDs;
 //   * longest first: sequences in decreasing order of split count (then of
 //     pages per split, then by index), each sequence's items by split, row
 //     group and KV head, so a call that takes more than one wave of
 //     workgroups starts its long items first (a sequence with more than the
 //     minimum pages per split has about S splits, the most there are);
-// and lists the packed rows for the merge in the same sequence order: rows
-// of sequences with many splits, whose merge reads the most, first, then the
-// rows with at most kMergeLightSplits splits, which the merge takes one wave
-// per (row, head) instead of a workgroup.  Which
-// items exist, and what each computes, is exactly as before: a sequence's
-// splits depend only on its own context, the plan and the call's split count,
-// so its outputs do not depend on the other sequences of the call (page
-// "perf(qwen35): retain speculation during paged prefill", Correctness
-// failure found during qualification).
+//   * the packed rows for the merge in the same sequence order: rows of
+//     sequences with many splits, whose merge reads the most, first, then
+//     the rows with at most kMergeLightSplits splits, which the merge takes
+//     one wave per (row, head) instead of a workgroup.
+// Sequences are taken in index order while their rows fit the packed
+// capacity and their items the grid (only overlapping bad cu_rows entries
+// can exceed either).  Which items a sequence has, and what each computes,
+// follow from that sequence's context, the plan and the call's split count
+// alone, so its outputs do not depend on the other sequences of the call
+// (page "perf(qwen35): retain speculation during paged prefill", Correctness
+// failure found during qualification); the order only decides when each
+// item runs.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
