@@ -19,7 +19,7 @@ import synthetic as S
 import speculative_decoding_verify_kv_amd as va
 from speculative_decoding_verify_kv_amd import device as vdev
 
-from .gpu_util import check_parity, ensure_lib, run_gpu, say
+from .gpu_util import check_parity, ensure_lib, say
 
 pytestmark = pytest.mark.gpu
 
@@ -37,19 +37,31 @@ def _dirty_workspace(nbytes):
     return ws
 
 
-def _call(w, plan, dev, ws, num_splits, out_dtype, ragged):
+def _outputs(w, out_dtype, ragged):
     import torch
 
     rows = w.total_rows if ragged else w.num_seqs * w.B
     dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[out_dtype]
     out = torch.full((rows, w.H, w.D), float("nan"), dtype=dt, device="cuda")
     lse = torch.full((rows, w.H), float("nan"), dtype=torch.float32, device="cuda")
+    return out, lse
+
+
+def _launch(plan, dev, ws, num_splits, out, lse, ragged, stream=None):
     args = (dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"], dev["block_table"],
             dev["ctx_lens"])
     if ragged:
-        va.verify_attn_run_ragged(plan, *args, dev["cu_rows"], dev["parent"], num_splits, out, lse, ws)
+        va.verify_attn_run_ragged(plan, *args, dev["cu_rows"], dev["parent"], num_splits, out, lse, ws,
+                                  stream=stream)
     else:
-        va.verify_attn_run(plan, *args, dev["parent"], num_splits, out, lse, ws)
+        va.verify_attn_run(plan, *args, dev["parent"], num_splits, out, lse, ws, stream=stream)
+
+
+def _call(w, plan, dev, ws, num_splits, out_dtype, ragged):
+    import torch
+
+    out, lse = _outputs(w, out_dtype, ragged)
+    _launch(plan, dev, ws, num_splits, out, lse, ragged)
     torch.cuda.synchronize()
     flags = va.verify_attn_read_flags(plan, ws)
     return out.float().cpu().double().numpy(), lse.cpu().double().numpy(), flags
@@ -101,3 +113,39 @@ def test_ragged_calls_share_one_workspace():
     items = {"mixed": S.mixed_lowering(), "small": small}
     _run_sequence(items, [("mixed", 0), ("small", 0), ("mixed", 4), ("small", 2), ("mixed", 0)], "f16",
                   ragged=True)
+
+
+def test_concurrent_streams_distinct_workspaces():
+    """Three calls (two uniform plans and a ragged one) issued round-robin on
+    three streams, 6 times each with no synchronisation in between, each call
+    with its own workspace: the calls may overlap on the device, and each
+    stream's last result equals the same call run alone, bit for bit
+    (concurrent calls need distinct workspaces, nothing else)."""
+    import torch
+
+    items = [
+        (S.make_workload("cs_a", ctx_lens=[6000], B=16, H=24, KVH=4, D=256, q_dtype="bf16", kv_dtype="q8_0",
+                         seed=81, permute=True), False),
+        (S.make_workload("cs_b", ctx_lens=[2500, 900, 4100], B=4, H=8, KVH=1, D=64, q_dtype="f32",
+                         kv_dtype="f16", seed=82, permute=True), False),
+        (S.mixed_lowering(seed=83, prefill=(24,), prefill_ctx=(800,), direct_ctx=(5000, 1500), tree_ctx=3000,
+                          n_direct=2, n_tree=4), True),
+    ]
+    runs = []
+    for w, ragged in items:
+        plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f32"), 0, 0)
+        dev = vdev.to_device(w)
+        alone = _call(w, plan, dev, vdev.workspace(plan), 0, "f32", ragged)
+        assert alone[2] == 0
+        out, lse = _outputs(w, "f32", ragged)
+        runs.append((w, ragged, plan, dev, vdev.workspace(plan), out, lse, alone, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    say(f"[case] {len(runs)} streams x 6 calls, no sync in between")
+    for _ in range(6):
+        for w, ragged, plan, dev, ws, out, lse, alone, st in runs:
+            _launch(plan, dev, ws, 0, out, lse, ragged, stream=st)
+    torch.cuda.synchronize()
+    for w, ragged, plan, dev, ws, out, lse, alone, st in runs:
+        assert va.verify_attn_read_flags(plan, ws) == 0
+        assert np.array_equal(out.float().cpu().double().numpy(), alone[0]), w.name
+        assert np.array_equal(lse.cpu().double().numpy(), alone[1]), w.name
