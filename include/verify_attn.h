@@ -336,12 +336,18 @@ va_status verify_attn_append_kv(const va_plan* plan, const void* k_new, const vo
  * written to any pool, and new_ctx[s] = ctx_lens[s] for every s.
  *   accepted, n_accepted     [num_seqs, B] / [num_seqs] int32, device
  *   parent                   [num_seqs, B] or NULL (chain), device
- *   new_ctx                  [num_seqs] int32 output, device, optional (NULL)
+ *   new_ctx                  [num_seqs] int32 output, device, optional (NULL);
+ *                            not ctx_lens itself (VA_EINVAL)
  *   workspace                device, 256-byte aligned, at least
  *                            verify_attn_promote_workspace_bytes(plan) bytes:
  *                            flag word at byte 0, this call's check word at
  *                            byte 4, staging of the accepted rows after 256
  * Sources and destinations may overlap (the rows are staged first).
+ * Sequences must not share the pages that hold their drafted slots (as for
+ * verify_attn_append_kv).  A batch of at most 256 (sequence, path slot)
+ * pairs is one launch (a workgroup per sequence and KV head, each repeating
+ * the batch's checks and staging its rows in LDS); a larger one is three
+ * launches that stage the rows in the workspace.
  */
 va_status verify_attn_promote_kv(const va_plan* plan, const int32_t* accepted, const int32_t* n_accepted,
                                  const int32_t* parent, void* k_pool, void* v_pool, void* k_scale, void* v_scale,

@@ -521,6 +521,7 @@ va_status verify_attn_promote_kv(const va_plan* plan, const int32_t* accepted, c
     return VA_EINVAL;
   }
   if ((p.has_parent != 0) != (parent != nullptr)) return VA_EINVAL;
+  if (new_ctx && new_ctx == ctx_lens) return VA_EINVAL;  // rows still read ctx_lens while new_ctx is written
   if (workspace_bytes < verify_attn_promote_workspace_bytes(plan)) return VA_EWORKSPACE;
   va::PromoteParams pp;
   memset(&pp, 0, sizeof pp);

@@ -142,6 +142,8 @@ hipError_t launch_schedule(const ScheduleParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 size_t promote_row_bytes(int D, int kv_dtype);
 hipError_t launch_promote(const PromoteParams& p, hipStream_t stream);
+// True when the call runs as one launch (the batch's staging fits in LDS).
+bool promote_one_launch(const PromoteParams& p);
 
 }  // namespace va
 

@@ -47,11 +47,13 @@ def paths(w, pick):
     return acc, n
 
 
-def gpu_promote(w, acc, n):
+def gpu_promote(w, acc, n, ws_out=None):
     dev = vdev.to_device(w)
     plan = va.verify_attn_plan(vdev.problem_for(w), 1, 0)
     wsb = va.verify_attn_promote_workspace_bytes(plan)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    if ws_out is not None:
+        ws_out.append(ws)
     acc_d = torch.from_numpy(np.ascontiguousarray(acc)).cuda()
     n_d = torch.from_numpy(np.ascontiguousarray(n)).cuda()
     new_ctx = torch.full((w.num_seqs,), -7, dtype=torch.int32, device="cuda")
@@ -134,3 +136,35 @@ def test_promote_then_verify_over_the_promoted_prefix():
         dv[name] = dev[name]
     got = run_gpu(wv, 0, "f32", dev=dv)[0]
     check_parity(got, ref, "f32", "verify after promotion")
+
+
+# A batch of at most 256 (sequence, path slot) pairs is one launch; a larger
+# one is three launches, whose status word (workspace bytes 4..7) records a
+# failed check.
+ONE_LAUNCH_PAIRS = 256
+
+
+@pytest.mark.parametrize("nseq", [6, 26])
+def test_promote_one_and_three_launch_forms(nseq):
+    ctxs = [40 + 37 * i for i in range(nseq)]
+    w = tree_case("q8_0", 256, seed=12, ctxs=ctxs)
+    one = nseq * w.B <= ONE_LAUNCH_PAIRS
+    assert one == (nseq == 6)
+    say(f"[case] promote {nseq} sequences, {nseq * w.B} path slots ({'one launch' if one else 'three launches'})")
+    acc, n = paths(w, lambda s: path_to(w.parent[s], w.B - 1 - (s % 5)))
+    n[3] = 0  # one sequence accepts nothing
+    k, v, ks, vs, new_ctx = oracle.promote_kv(w, acc, n)
+    dev, got_ctx, flags = gpu_promote(w, acc, n)
+    assert flags == 0
+    assert np.array_equal(got_ctx, new_ctx)
+    assert _same_pools(dev, k, v, ks, vs)
+    # a bad path in the last sequence: nothing is written in either form
+    acc_bad = acc.copy()
+    acc_bad[nseq - 1, 0] = w.B
+    wss = []
+    dev, got_ctx, flags = gpu_promote(w, acc_bad, n, wss)
+    assert flags & va.VA_FLAG_BAD_PATH
+    assert np.array_equal(got_ctx, w.ctx_lens)
+    assert _same_pools(dev, w.k_pool, w.v_pool, w.k_scale, w.v_scale)
+    status = int(wss[0][4:8].cpu().numpy().view(np.uint32)[0])
+    assert status == (0 if one else int(va.VA_FLAG_BAD_PATH))

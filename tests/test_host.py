@@ -244,6 +244,7 @@ def test_promote_workspace_and_rejections(lib):
     assert promote_status(plan, parent=FAKE) == va.VA_EINVAL          # has_parent == 0
     assert promote_status(plan, k_scale=None) == va.VA_EINVAL
     assert promote_status(plan, new_ctx=FAKE + 2) == va.VA_EINVAL
+    assert promote_status(plan, new_ctx=FAKE + 64, ctx_lens=FAKE + 64) == va.VA_EINVAL  # new_ctx is ctx_lens
     assert promote_status(plan, workspace=FAKE + 128) == va.VA_EINVAL
     plan_p = va.verify_attn_plan_for_cus(qwen(has_parent=True), 8, 256)
     assert promote_status(plan_p) == va.VA_EINVAL                     # parent required
