@@ -83,6 +83,9 @@ va_status check_problem(const va_problem* p) {
   if (p->max_ctx < p->rows_per_seq) return VA_EINVAL;
   if ((int64_t)p->max_ctx > (int64_t)p->max_pages_per_seq * va::kPage) return VA_EINVAL;
   if (rows_capacity(*p) * p->num_q_heads > INT32_MAX) return VA_EUNSUPPORTED;
+  // one split's partials (rows x heads x head_dim floats) are addressed by
+  // 32-bit byte offsets
+  if (rows_capacity(*p) * p->num_q_heads * p->head_dim * (int64_t)sizeof(float) > INT32_MAX) return VA_EUNSUPPORTED;
   // ragged calls list their work per sequence (sequence, KV head and split
   // packed with the row group in 8-byte entries)
   if (ragged(*p) && (p->num_seqs > va::kMaxSchedSeqs || p->num_kv_heads > 256)) return VA_EUNSUPPORTED;

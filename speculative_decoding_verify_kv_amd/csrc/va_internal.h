@@ -95,6 +95,12 @@ struct AppendParams {
   int32_t new_dtype, kv_dtype;
 };
 
+// Cache-policy operand of the buffer load / store builtins for the bits a
+// relaxed system-scope atomic access gets on gfx950 (sc0 sc1), and the
+// descriptor flags of a raw buffer (no swizzle, 32-bit format).
+constexpr int kSystemScopeBits = 17;
+constexpr int kRawBufferFlags = 0x00020000;
+
 struct PromoteParams {
   const int32_t* accepted;   // [num_seqs, B] root-first path rows
   const int32_t* n_accepted; // [num_seqs]

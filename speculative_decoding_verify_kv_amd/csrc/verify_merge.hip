@@ -71,6 +71,25 @@ __device__ __forceinline__ void store_row(const MergeParams& p, int64_t R, int l
     p.lse[R] = nan_row ? __builtin_nanf("") : 0.6931471805599453f * (M + __builtin_log2f(L));
 }
 
+// Partials are read with system-scope loads (sc0 sc1, the bits of a relaxed
+// system-scope atomic load), as the partial kernel writes them: no L2 line
+// left from an earlier use of the workspace is read in their place.  A
+// split's row of one (row, head) is D floats; lane l reads entries E l ..
+// E l + E - 1.
+template <typename V>
+__device__ __forceinline__ V load_partial(const float* row, int lane) {
+  constexpr int E = sizeof(V) / sizeof(float);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), 0, 64 * E * (int)sizeof(float), kRawBufferFlags);
+  if constexpr (E == 4) return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, kSystemScopeBits));
+  else if constexpr (E == 2) return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * lane, 0, kSystemScopeBits));
+  else return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, 0, kSystemScopeBits));
+}
+
+__device__ __forceinline__ float load_header(const float* x) {
+  return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // One wave merges (row, head) R alone: for ragged rows whose sequence has at
 // most kMergeLightSplits splits.  Same arithmetic, in the same order, as the
 // workgroup form below gives such a row (each of its waves then holds at
@@ -84,7 +103,6 @@ __device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, 
   const int S = p.S;
   const int Sr = max(1, min(S, *reinterpret_cast<const __attribute__((address_space(4))) int*>(
                                     (uintptr_t)(p.part_n + R))));
-  const float* base = p.part_o + R * D + E * lane;
   const int64_t kstride = p.nrows * D;
   float mh[HJ], lh[HJ];
 #pragma unroll
@@ -93,8 +111,8 @@ __device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, 
     mh[j] = -INFINITY;
     lh[j] = 0.f;
     if (k < Sr) {
-      mh[j] = p.part_m[(int64_t)k * p.nrows + R];
-      lh[j] = p.part_l[(int64_t)k * p.nrows + R];
+      mh[j] = load_header(p.part_m + (int64_t)k * p.nrows + R);
+      lh[j] = load_header(p.part_l + (int64_t)k * p.nrows + R);
     }
   }
   float M = -INFINITY;
@@ -121,7 +139,7 @@ __device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, 
     vec v[kMergeBatch];
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b)
-      v[b] = *reinterpret_cast<const vec*>(base + (int64_t)min(k0 + b, S - 1) * kstride);
+      v[b] = load_partial<vec>(p.part_o + (int64_t)min(k0 + b, S - 1) * kstride + R * D, lane);
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
       const int k = k0 + b;  // wave-uniform
@@ -185,11 +203,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   const int Sr = !p.part_n ? S
                            : max(1, min(S, *reinterpret_cast<const __attribute__((address_space(4))) int*>(
                                                (uintptr_t)(p.part_n + R))));
-  const float* base = p.part_o + R * D + E * lane;
   const int64_t kstride = p.nrows * D;
 
   auto load = [&](int k) __attribute__((always_inline)) -> vec {
-    return *reinterpret_cast<const vec*>(base + (int64_t)min(k, S - 1) * kstride);  // clamped: weight 0 below
+    return load_partial<vec>(p.part_o + (int64_t)min(k, S - 1) * kstride + R * D, lane);  // clamped: weight 0 below
   };
   // Split headers, read by wave 0 alone (lane: splits lane + 64 j) ahead of
   // its partial rows, so the weights are ready first; they reach the other
@@ -203,8 +220,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
       mh[j] = -INFINITY;
       lh[j] = 0.f;
       if (k < Sr) {
-        mh[j] = p.part_m[(int64_t)k * p.nrows + R];
-        lh[j] = p.part_l[(int64_t)k * p.nrows + R];
+        mh[j] = load_header(p.part_m + (int64_t)k * p.nrows + R);
+        lh[j] = load_header(p.part_l + (int64_t)k * p.nrows + R);
       }
     }
   }

@@ -1112,15 +1112,27 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
         if (dq == 0 && g4 == 0 && p.lse)
           p.lse[Rg] = any_poison ? __builtin_nanf("") : kLn2 * (mref[nt] + __builtin_log2f(Lrow));
       } else {
-        float* po = p.part_o + ((int64_t)split * p.nrows + Rg) * D;
+        // System-scope stores (the cache bits, sc0 sc1, of a relaxed
+        // system-scope atomic store), matched by the merge's system-scope
+        // loads: the partials reach memory without waiting in an XCD's L2
+        // for the end-of-kernel write-back, and no L2 line left from an
+        // earlier use of the workspace can be read in their place.  One
+        // split's block (nrows * D floats, below 2^31 bytes: checked at plan
+        // time) is the descriptor's range; lanes address it by byte offset.
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            p.part_o + (int64_t)split * p.nrows * D, 0, p.nrows * D * (int)sizeof(float), kRawBufferFlags);
 #pragma unroll
         for (int mt = 0; mt < G::MTO; ++mt) {
           const int dim = dq * G::DO + 16 * mt + 4 * g4;
-          *reinterpret_cast<f32x4*>(po + dim) = any_poison ? f32x4{__builtin_nanf(""), 0.f, 0.f, 0.f} : oacc[mt][nt];
+          const f32x4 val = any_poison ? f32x4{__builtin_nanf(""), 0.f, 0.f, 0.f} : oacc[mt][nt];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, val), rs, (Rg * D + dim) * 4, 0,
+                                                 kSystemScopeBits);
         }
         if (dq == 0 && g4 == 0) {
-          p.part_m[(int64_t)split * p.nrows + Rg] = any_poison ? 0.f : mref[nt];
-          p.part_l[(int64_t)split * p.nrows + Rg] = any_poison ? __builtin_nanf("") : Lrow;
+          __hip_atomic_store(p.part_m + (int64_t)split * p.nrows + Rg, any_poison ? 0.f : mref[nt], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(p.part_l + (int64_t)split * p.nrows + Rg, any_poison ? __builtin_nanf("") : Lrow,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
       }
     }

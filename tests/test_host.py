@@ -311,6 +311,9 @@ def test_ragged_plan_sizes_by_packed_rows(lib):
     assert plan_status(qwen(num_seqs=2048, rows_per_seq=1, max_total_rows=2048)) == va.VA_OK
     assert plan_status(qwen(num_seqs=2049, rows_per_seq=1, max_total_rows=2049)) == va.VA_EUNSUPPORTED
     assert plan_status(qwen(num_seqs=2049, rows_per_seq=1)) == va.VA_OK  # uniform plans have no such list
+    # one split's partials (rows x heads x head_dim floats) must stay below 2^31 bytes
+    assert plan_status(qwen(num_seqs=1365, rows_per_seq=64, max_ctx=64)) == va.VA_OK       # 2,096,640 row-heads
+    assert plan_status(qwen(num_seqs=1366, rows_per_seq=64, max_ctx=64)) == va.VA_EUNSUPPORTED  # 2,098,176
     # capacity above num_seqs * rows_per_seq, or negative
     assert plan_status(qwen(num_seqs=2, rows_per_seq=10, max_total_rows=21)) == va.VA_EINVAL
     assert plan_status(qwen(max_total_rows=-1)) == va.VA_EINVAL
