@@ -170,6 +170,10 @@ typedef struct {
  *   out_plan         (host) receives the plan; NULL on error
  *   workspace_bytes  (host, may be NULL) receives the workspace size
  * Returns VA_OK, VA_EINVAL or VA_EUNSUPPORTED (or VA_EHIP if the device query fails).
+ * VA_EUNSUPPORTED besides shapes and dtypes the kernels do not implement: one
+ * split's partials (row capacity x num_q_heads x head_dim fp32 values) of
+ * 2^31 bytes or more (their stores and loads take 32-bit offsets), and
+ * ragged plans of more than 2,048 sequences or 256 KV heads.
  */
 va_status verify_attn_plan(const va_problem* problem, int32_t num_splits, int32_t device_ordinal,
                            va_plan** out_plan, size_t* workspace_bytes);
