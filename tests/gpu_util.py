@@ -81,7 +81,7 @@ def check_parity(got, ref, out_dtype, what=""):
     say(f"  parity {what}: rel_l2={rel:.3e} max_abs={mx:.3e} ({out_dtype})")
     assert np.all(np.isfinite(got)), what
     # max-abs gate on top of the output format's own rounding of the exact
-    # value: outputs above 1 in bf16 (or above 4 in fp16) round by more than
+    # value: outputs above 1 in bf16 (or from 8 up in fp16) round by more than
     # 2e-3 on their own
     excess = np.abs(got - ref) - half_ulp(ref, out_dtype)
     assert excess.max() <= MAX_ABS, (what, mx, float(excess.max()))
