@@ -245,10 +245,9 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
   pp.flags = reinterpret_cast<uint32_t*>(ws);
   float* part = reinterpret_cast<float*>(ws + va::kHeaderBytes);
   pp.part_o = part;
-  pp.part_m = part + (int64_t)plan->max_splits * nrows * p.head_dim;
-  pp.part_l = pp.part_m + (int64_t)plan->max_splits * nrows;
+  pp.part_ml = reinterpret_cast<uint64_t*>(part + (int64_t)plan->max_splits * nrows * p.head_dim);
   // ragged calls split each sequence by its own context (see kMinSplitPages)
-  pp.part_n = ragged(p) ? reinterpret_cast<int32_t*>(pp.part_l + (int64_t)plan->max_splits * nrows) : nullptr;
+  pp.part_n = ragged(p) ? reinterpret_cast<int32_t*>(pp.part_ml + (int64_t)plan->max_splits * nrows) : nullptr;
   if (ragged(p)) {
     char* sched = ws + sched_offset(p, plan->max_splits);
     pp.item_count = reinterpret_cast<const int32_t*>(sched);
@@ -279,8 +278,7 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
 va::MergeParams merge_params(const va::PartialParams& pp, void* out, float* lse) {
   va::MergeParams mp;
   mp.part_o = pp.part_o;
-  mp.part_m = pp.part_m;
-  mp.part_l = pp.part_l;
+  mp.part_ml = pp.part_ml;
   mp.part_n = pp.part_n;
   mp.out = out;
   mp.lse = lse;
@@ -413,8 +411,7 @@ va_status verify_attn_run_noalloc(const va_plan* plan, const void* q, const void
   const int64_t nrows = pp.nrows;
   float* part = static_cast<float*>(base);
   pp.part_o = part;
-  pp.part_m = part + (int64_t)S * nrows * p.head_dim;
-  pp.part_l = pp.part_m + (int64_t)S * nrows;
+  pp.part_ml = reinterpret_cast<uint64_t*>(part + (int64_t)S * nrows * p.head_dim);
   pp.part_n = nullptr;
   pp.flags = flags;
   hipStream_t s = static_cast<hipStream_t>(stream);

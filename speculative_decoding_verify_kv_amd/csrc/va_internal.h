@@ -47,8 +47,7 @@ struct PartialParams {
   void* out;              // direct mode output
   float* lse;             // direct mode lse (may be NULL)
   float* part_o;          // [S][nrows][D]
-  float* part_m;          // [S][nrows]  (log2 units)
-  float* part_l;          // [S][nrows]
+  uint64_t* part_ml;      // [S][nrows] (m, l) pairs: m (log2 units) in the low word, l in the high word
   int32_t* part_n;        // ragged calls: [nrows] splits that hold keys of the row's sequence (written by split 0); else NULL
   const int2* items;      // ragged calls: the work list (sequence, row group << 16 | split << 8 | KV head)
   const int32_t* item_count;  // ragged calls: entries of `items` in use
@@ -68,8 +67,7 @@ struct PartialParams {
 
 struct MergeParams {
   const float* part_o;
-  const float* part_m;
-  const float* part_l;
+  const uint64_t* part_ml;
   const int32_t* part_n;
   void* out;
   float* lse;

@@ -17,10 +17,10 @@
 // ...; it issues the loads of up to 4 of its split rows at once (16 bytes
 // per lane each at D = 256) right away, so the partial rows are in flight
 // while the weights are formed.  Wave 0 alone loads the split headers, just
-// before its rows (lane: splits lane, lane + 64, ...; each is a lone 4-byte
-// read from its own cache line, so one wave's worth is cheaper than eight),
-// and hands the weights to the other waves through LDS.  The 8 waves' sums
-// meet in LDS.
+// before its rows (lane: splits lane, lane + 64, ...; each split's (m, l)
+// is one 8-byte pair, a lone read from its own cache line, so one wave's
+// worth is cheaper than eight), and hands the weights to the other waves
+// through LDS.  The 8 waves' sums meet in LDS.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -86,8 +86,11 @@ __device__ __forceinline__ V load_partial(const float* row, int lane) {
   else return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, 0, kSystemScopeBits));
 }
 
-__device__ __forceinline__ float load_header(const float* x) {
-  return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+// A split's (m, l) pair of one (row, head): one 8-byte system-scope load.
+__device__ __forceinline__ void load_header(const uint64_t* x, float& m, float& l) {
+  const uint64_t ml = __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  m = __builtin_bit_cast(float, (uint32_t)ml);
+  l = __builtin_bit_cast(float, (uint32_t)(ml >> 32));
 }
 
 // One wave merges (row, head) R alone: for ragged rows whose sequence has at
@@ -111,8 +114,7 @@ __device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, 
     mh[j] = -INFINITY;
     lh[j] = 0.f;
     if (k < Sr) {
-      mh[j] = load_header(p.part_m + (int64_t)k * p.nrows + R);
-      lh[j] = load_header(p.part_l + (int64_t)k * p.nrows + R);
+      load_header(p.part_ml + (int64_t)k * p.nrows + R, mh[j], lh[j]);
     }
   }
   float M = -INFINITY;
@@ -220,8 +222,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
       mh[j] = -INFINITY;
       lh[j] = 0.f;
       if (k < Sr) {
-        mh[j] = load_header(p.part_m + (int64_t)k * p.nrows + R);
-        lh[j] = load_header(p.part_l + (int64_t)k * p.nrows + R);
+        load_header(p.part_ml + (int64_t)k * p.nrows + R, mh[j], lh[j]);
       }
     }
   }

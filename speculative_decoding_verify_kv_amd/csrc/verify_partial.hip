@@ -1129,10 +1129,10 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
                                                  kSystemScopeBits);
         }
         if (dq == 0 && g4 == 0) {
-          __hip_atomic_store(p.part_m + (int64_t)split * p.nrows + Rg, any_poison ? 0.f : mref[nt], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_SYSTEM);
-          __hip_atomic_store(p.part_l + (int64_t)split * p.nrows + Rg, any_poison ? __builtin_nanf("") : Lrow,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          // the row's (m, l) as one 8-byte pair
+          const float mv = any_poison ? 0.f : mref[nt], lv = any_poison ? __builtin_nanf("") : Lrow;
+          const uint64_t ml = (uint64_t)__builtin_bit_cast(uint32_t, mv) | (uint64_t)__builtin_bit_cast(uint32_t, lv) << 32;
+          __hip_atomic_store(p.part_ml + (int64_t)split * p.nrows + Rg, ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         }
       }
     }
