@@ -19,8 +19,9 @@
 //    word, (2) check every (sequence, path node) and gather the accepted rows
 //    into workspace staging, (3) if no check failed, scatter the staging rows
 //    to their destination slots and write new_ctx.
-// One wave per (sequence, path slot, KV head, K or V): lane l moves head_dim
-// entries 4l .. 4l + 3 and lane b < D/32 the scale of block b.
+// The three-launch form runs one wave per (sequence, path slot, KV head, K or
+// V): lane l moves head_dim entries 4l .. 4l + 3 and lane b < D/32 the scale
+// of block b (the one-launch form's lanes are described at its kernel).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
