@@ -16,6 +16,9 @@
 //     group and KV head, so a call that takes more than one wave of
 //     workgroups starts its long items first (a sequence with more than the
 //     minimum pages per split has about S splits, the most there are);
+//   * a sequence of at most kThinRows (row, head) pairs has its items marked
+//     thin (when the plan's row groups are larger), and the partial kernel
+//     runs them with its 32-row body;
 //   * the packed rows for the merge in the same sequence order: rows of
 //     sequences with many splits, whose merge reads the most, first, then
 //     the rows with at most kMergeLightSplits splits, which the merge takes
@@ -43,6 +46,12 @@ constexpr int kSortSeqs = 256;  // sequences ordered by size up to this count; b
 struct SeqInfo {
   int rows, a, groups, splits, items, pp;
 };
+
+// The first word of a sequence's items: its index, and kItemThin for a
+// sequence the partial kernel runs with its 32-row body.
+__device__ __forceinline__ int item_seq_word(const ScheduleParams& p, int s, int rows) {
+  return s | (p.qrows > kThinRows && rows * p.G <= kThinRows ? kItemThin : 0);
+}
 
 // cu: the call's cu_rows and ctx: its ctx_lens, staged in LDS
 __device__ __forceinline__ SeqInfo seq_info(const ScheduleParams& p, const int* cu, const int* ctxs, int s) {
@@ -194,7 +203,7 @@ __global__ __launch_bounds__(kSchedThreads) void ragged_schedule_kernel(const Sc
     const int per_split = q.groups * p.KVH;
     const int split = t / per_split, rem = t - split * per_split;
     const int g = rem / p.KVH, kvh = rem - g * p.KVH;
-    p.items[i] = make_int2(s, (g << 16) | (split << 8) | kvh);
+    p.items[i] = make_int2(item_seq_word(p, s, q.rows), (g << 16) | (split << 8) | kvh);
   }
   // the packed rows to merge, in the same sequence order
   for (int k = tid; k < total_rows; k += kSchedThreads) {
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(64) void ragged_schedule_wave_kernel(const Schedule
   for (int r = 0; r < n; ++r) {
     const int cnt = __builtin_amdgcn_readlane(items_r, r);
     const int base = __builtin_amdgcn_readlane(pre_i, r);
-    const int sq = __builtin_amdgcn_readlane(s, r);
+    const int sq = item_seq_word(p, __builtin_amdgcn_readlane(s, r), __builtin_amdgcn_readlane(rows_r, r));
     const int groups_q = __builtin_amdgcn_readlane(groups_r, r);
     // entry t of the sequence is (split, group, KV head) = t in the mixed
     // radix (groups, KVH), counted incrementally: lane t starts at its own

@@ -30,6 +30,13 @@ constexpr int kMaxSchedSeqs = 2048;
 // one wave per (row, head) rather than one workgroup.
 constexpr int kMergeLightSplits = 8;
 
+// Ragged work-list entries: (sequence | flags, row group << 16 | split << 8 |
+// KV head).  kItemThin marks a sequence of at most kThinRows (row, head)
+// pairs, which the partial kernel runs with its 32-row body.
+constexpr int kItemSeqMask = 0x3fffffff;
+constexpr int kItemThin = 0x40000000;
+constexpr int kThinRows = 32;
+
 // Kernel-side dtype codes (same values as va_dtype).
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kQ8 = 3 };
 

@@ -276,8 +276,10 @@ __device__ __forceinline__ u32x4 tail_mask(int first, int end) {
 // SQ: split each sequence by its own context with at least kMinSplitPages
 // pages per split (ragged calls, whose sequences differ widely in length);
 // otherwise every sequence takes S equal splits.
+// One workgroup's work in the LDS block `smem` (16 NT rows of the group list
+// per workgroup).
 template <int D, int KVT, int NT, bool SQ>
-__global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const PartialParams p) {
+__device__ __forceinline__ void partial_body(const PartialParams p, char* smem) {
   using G = Geo<D, KVT>;
   using L = Lay<D, KVT, NT>;
   static_assert(NT % 2 == 0, "the score waves take half the rows each");
@@ -286,7 +288,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
   constexpr int KSTEPS = G::KSTEPS;
   constexpr int NDMA = G::NDMA;
   constexpr int QROWS = 16 * NT;
-  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
   const int tid = threadIdx.x;
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
     if ((int)blockIdx.x >= cnt[0]) return;
     const auto* it =
         reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.items + blockIdx.x));
-    s = it[0];
+    s = it[0] & kItemSeqMask;
     const int packed = it[1];
     rg = packed >> 16;
     split = (packed >> 8) & 255;
@@ -1141,6 +1142,31 @@ __global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const 
       if (bits) atomicOr(p.flags, bits);
     }
   }
+}
+
+// The kernel.  A ragged entry the work-list pass marked thin (a sequence of
+// at most 32 (row, head) pairs) runs the 32-row body, as a uniform call with
+// so few rows would: a larger body would carry 64 or more copied rows through
+// every MFMA and softmax.  Rows do not depend on the body that computes them
+// (each row's scores, softmax and P.V are its own; the rare rescale is taken
+// for the group's distinct rows, the same in either body), so the choice
+// changes no value.
+template <int D, int KVT, int NT, bool SQ>
+__global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const PartialParams p) {
+  constexpr bool kThinBody = SQ && NT > 2;
+  constexpr int kBytes = kThinBody && Lay<D, KVT, 2>::BYTES > Lay<D, KVT, NT>::BYTES ? Lay<D, KVT, 2>::BYTES
+                                                                                     : Lay<D, KVT, NT>::BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[kBytes];
+  if constexpr (kThinBody) {
+    const auto* cnt = reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)p.item_count);
+    const auto* it =
+        reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.items + blockIdx.x));
+    if ((int)blockIdx.x < cnt[0] && (it[0] & kItemThin) != 0) {
+      partial_body<D, KVT, 2, true>(p, smem);
+      return;
+    }
+  }
+  partial_body<D, KVT, NT, SQ>(p, smem);
 }
 
 }  // namespace

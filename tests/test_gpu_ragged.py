@@ -324,7 +324,9 @@ def _work_list_model(w, cu, S, plan, ctx_lens=None):
     those ordered by split count, then pages per split, descending (ties by
     index); each sequence's entries by split, row group, KV head; then its
     packed rows for the merge, and how many of those rows have more than 8
-    splits."""
+    splits.  An entry's first word is the sequence, with bit 30 set for a
+    sequence of at most 32 (row, head) pairs when the plan's row groups are
+    larger."""
     info = plan.info()
     G = w.H // w.KVH
     cap_rows = plan.problem.max_total_rows
@@ -357,10 +359,13 @@ def _work_list_model(w, cu, S, plan, ctx_lens=None):
     for key, s, a, rows, groups, splits, n in order:
         if not n:  # not taken, or nothing to do
             continue
+        # a sequence of at most 32 (row, head) pairs runs the 32-row body
+        thin = info.rows_per_group > 32 and rows * G <= 32
+        word = s | (0x40000000 if thin else 0)
         for sp in range(splits):
             for g in range(groups):
                 for kvh in range(w.KVH):
-                    items.append((s, (g << 16) | (sp << 8) | kvh))
+                    items.append((word, (g << 16) | (sp << 8) | kvh))
         merge_rows.extend(range(a, a + rows))
         heavy += rows if splits > 8 else 0
     return items, merge_rows, heavy
