@@ -48,15 +48,18 @@ NPOOLS = 8
 
 
 def build_digest(root, src):
-    """sha256 of a kernel source followed by its own compiler flags (a newline,
-    then the flags joined by spaces): what a counter summary was taken on."""
+    """sha256 of a kernel source, a newline, the shared header va_internal.h
+    that every kernel source compiles in, a newline, and the source's own
+    compiler flags joined by spaces: what a counter summary was taken on."""
     import hashlib
 
     from speculative_decoding_verify_kv_amd import build as vbuild
 
-    data = open(os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc", src), "rb").read()
+    csrc = os.path.join(root, "speculative_decoding_verify_kv_amd", "csrc")
+    data = open(os.path.join(csrc, src), "rb").read()
+    header = open(os.path.join(csrc, "va_internal.h"), "rb").read()
     flags = " ".join(vbuild.PER_SOURCE_FLAGS.get(src, []))
-    return hashlib.sha256(data + b"\n" + flags.encode()).hexdigest()
+    return hashlib.sha256(data + b"\n" + header + b"\n" + flags.encode()).hexdigest()
 
 
 def traffic_from_profile(root):
