@@ -475,3 +475,63 @@ def test_work_list_random_batches(seed):
     assert [tuple(x) for x in it.tolist()] == want_items
     flags = va.verify_attn_read_flags(plan, ws)
     assert bool(flags & va.VA_FLAG_BAD_ROWS) == expect_bad_rows
+
+
+def _thin_mix(seed):
+    """A ragged batch of one sequence with many rows (so the plan's row groups
+    hold 64 or 96 rows) beside 2-5 sequences of 0-8 rows, in a seeded head
+    layout, head_dim and KV type."""
+    rng = np.random.default_rng(7000 + seed)
+    H, KVH = [(24, 4), (8, 2), (16, 2), (4, 1)][seed % 4]
+    G = H // KVH
+    D = [64, 128, 256][seed % 3]
+    kv = ["q8_0", "f16"][(seed // 3) % 2]
+    n_small = int(rng.integers(2, 6))
+    big = int(rng.integers(33 // G + 2, 80 // G + 12))
+    rows = [big] + [int(x) for x in rng.integers(0, 9, size=n_small)]
+    order = rng.permutation(len(rows))
+    rows = [rows[i] for i in order]
+    ctx = [int(max(r, rng.integers(40, 3000))) for r in rows]
+    w = S.make_workload(f"thin_mix{seed}", ctx_lens=ctx, rows=rows, H=H, KVH=KVH, D=D, q_dtype="bf16",
+                        kv_dtype=kv, seed=7100 + seed, permute=True, spare_pages=3, poison=True)
+    return w
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_thin_entries_in_mixed_batches(seed):
+    """Sequences of at most 32 (row, head) pairs beside a long one run the
+    32-row partial body (the work-list pass marks their entries): every row
+    meets the oracle's gate, and every sequence's rows equal, bit for bit,
+    the same sequence run alone on the same plan (which body runs follows
+    from the sequence's own rows and the plan only)."""
+    import torch
+
+    w = _thin_mix(seed)
+    G = w.H // w.KVH
+    rows = np.diff(w.cu_rows).tolist()
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f32"), 0, 0)
+    qr = plan.info().rows_per_group
+    thin = [r for r in rows if 0 < r and r * G <= 32 and qr > 32]
+    say(f"[case] thin mix seed={seed} H={w.H}/{w.KVH} D={w.D} kv={w.kv_dtype} rows={rows} "
+        f"ctx={w.ctx_lens.tolist()} group={qr} thin={len(thin)}")
+    assert qr > 32 and thin  # the batch exercises both bodies
+    got, lse, flags, _ = run_ragged(w, 0, "f32", plan=plan)
+    assert flags == 0
+    n = w.total_rows
+    ref, lref = oracle.attention(w)
+    check_parity(got[:n], ref, "f32", f"thin mix {seed}")
+    assert np.abs(lse[:n] - lref).max() <= 2e-3
+    dev = vdev.to_device(w)
+    for s, r in enumerate(rows):
+        if r == 0:
+            continue
+        # sequence s alone: the other sequences get no rows
+        a = int(w.cu_rows[s])
+        cu = np.zeros(w.num_seqs + 1, np.int32)
+        cu[s + 1:] = r
+        q_alone = torch.zeros_like(dev["q"])
+        q_alone[:r] = dev["q"][a:a + r]
+        alone, alone_lse, aflags, _ = run_ragged(w, 0, "f32", plan=plan, dev=dev, cu_rows=cu, q=q_alone)
+        assert aflags == 0
+        assert np.array_equal(alone[:r], got[a:a + r]), f"sequence {s} ({r} rows) changed with the batch"
+        assert np.array_equal(alone_lse[:r], lse[a:a + r])
