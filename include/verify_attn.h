@@ -73,9 +73,7 @@
  * WORKSPACE
  *   verify_attn_plan reports workspace_bytes.  The first 256 bytes hold a
  *   uint32 flag word (kernels OR error bits into it); then the fp32 split
- *   partials and one int32 per (row, head): the number of splits that hold
- *   keys of the row's sequence (ragged calls); a ragged plan's workspace ends
- *   with the call's work list (what verify_attn_run_ragged's first kernel
+ *   partials; a ragged plan's workspace ends with the call's work list (what verify_attn_run_ragged's first kernel
  *   writes for the other two).  Zero the workspace once after allocating it;
  *   the flags stay set until verify_attn_read_flags clears them.
  *

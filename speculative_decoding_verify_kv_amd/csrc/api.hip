@@ -134,16 +134,15 @@ int64_t ragged_item_cap(const va_problem& p, const va::Tiling& t, int S) {
   return (int64_t)S * groups * p.num_kv_heads;
 }
 
-// Workspace: the flag header; with S > 1 the fp32 partials (O, m, l) of S
-// splits for every (row, head) and one int32 per (row, head); for a ragged
-// plan then, 256-byte aligned, the work list: two int32 counts (16 bytes),
-// the packed rows to merge (one int32 each, padded to 16 bytes) and the
-// entries (8 bytes each).
+// Workspace: the flag header; with S > 1 the fp32 partials (O, then the
+// (m, l) pairs) of S splits for every (row, head); for a ragged plan then,
+// 256-byte aligned, the work list: the int32 counts (16 bytes), the packed
+// rows to merge (one int32 each, with the row's split count, padded to 16
+// bytes) and the entries (8 bytes each).
 size_t sched_offset(const va_problem& p, int S) {
   const size_t nrows = (size_t)rows_capacity(p) * p.num_q_heads;
   if (S <= 1) return va::kHeaderBytes;
-  const size_t end =
-      va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float) + nrows * sizeof(int32_t);
+  const size_t end = va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float);
   return (end + 255) & ~(size_t)255;
 }
 
@@ -154,7 +153,7 @@ size_t workspace_for(const va_problem& p, const va::Tiling& t, int S) {
   if (ragged(p))
     return sched_offset(p, S) + 16 + merge_rows_bytes(p) + (size_t)ragged_item_cap(p, t, S) * sizeof(int2);
   if (S <= 1) return va::kHeaderBytes;
-  return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float) + nrows * sizeof(int32_t);
+  return va::kHeaderBytes + (size_t)S * nrows * ((size_t)p.head_dim + 2) * sizeof(float);
 }
 
 va_status make_plan(const va_problem* problem, int32_t num_splits, int32_t cus, va_plan** out_plan,
@@ -247,7 +246,6 @@ va::PartialParams partial_params(const va_plan* plan, const RunArgs& a, int32_t 
   pp.part_o = part;
   pp.part_ml = reinterpret_cast<uint64_t*>(part + (int64_t)plan->max_splits * nrows * p.head_dim);
   // ragged calls split each sequence by its own context (see kMinSplitPages)
-  pp.part_n = ragged(p) ? reinterpret_cast<int32_t*>(pp.part_ml + (int64_t)plan->max_splits * nrows) : nullptr;
   if (ragged(p)) {
     char* sched = ws + sched_offset(p, plan->max_splits);
     pp.item_count = reinterpret_cast<const int32_t*>(sched);
@@ -279,7 +277,6 @@ va::MergeParams merge_params(const va::PartialParams& pp, void* out, float* lse)
   va::MergeParams mp;
   mp.part_o = pp.part_o;
   mp.part_ml = pp.part_ml;
-  mp.part_n = pp.part_n;
   mp.out = out;
   mp.lse = lse;
   if (pp.items) {
@@ -412,7 +409,6 @@ va_status verify_attn_run_noalloc(const va_plan* plan, const void* q, const void
   float* part = static_cast<float*>(base);
   pp.part_o = part;
   pp.part_ml = reinterpret_cast<uint64_t*>(part + (int64_t)S * nrows * p.head_dim);
-  pp.part_n = nullptr;
   pp.flags = flags;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (va::launch_partial(pp, p.kv_dtype, plan->tiling.nt, s) != hipSuccess) return VA_EHIP;

@@ -19,7 +19,8 @@
 //   * a sequence of at most kThinRows (row, head) pairs has its items marked
 //     thin (when the plan's row groups are larger), and the partial kernel
 //     runs them with its 32-row body;
-//   * the packed rows for the merge in the same sequence order: rows of
+//   * the packed rows for the merge in the same sequence order, each with its
+//     sequence's split count (the merge weighs no later split): rows of
 //     sequences with many splits, whose merge reads the most, first, then
 //     the rows with at most kMergeLightSplits splits, which the merge takes
 //     one wave per (row, head) instead of a workgroup.
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kSchedThreads) void ragged_schedule_kernel(const Sc
     const int r = upper_rank(pre_rows, n, k);
     const int s = order[r];
     const SeqInfo q = seq_info(p, cu, ctxs, s);
-    p.merge_rows[k] = q.a + (k - (r > 0 ? pre_rows[r - 1] : 0));
+    p.merge_rows[k] = (q.a + (k - (r > 0 ? pre_rows[r - 1] : 0))) | ((q.splits - 1) << kMergeSplitShift);
   }
 }
 
@@ -300,7 +301,8 @@ __global__ __launch_bounds__(64) void ragged_schedule_wave_kernel(const Schedule
     const int nr = __builtin_amdgcn_readlane(rows_r, r);
     const int rbase = __builtin_amdgcn_readlane(pre_r, r);
     const int ar = __builtin_amdgcn_readlane(a_r, r);
-    for (int t = lane; t < nr; t += 64) p.merge_rows[rbase + t] = ar + t;
+    const int sr = __builtin_amdgcn_readlane(splits_r, r);
+    for (int t = lane; t < nr; t += 64) p.merge_rows[rbase + t] = (ar + t) | ((sr - 1) << kMergeSplitShift);
   }
 }
 

@@ -36,6 +36,12 @@ constexpr int kMergeLightSplits = 8;
 constexpr int kItemSeqMask = 0x3fffffff;
 constexpr int kItemThin = 0x40000000;
 constexpr int kThinRows = 32;
+// The merge's row list of a ragged call: each entry is a packed row with its
+// sequence's split count, row | (splits - 1) << kMergeSplitShift (rows stay
+// below 2^23: one split's partials are capped at 2^31 bytes at plan time).
+constexpr int kMergeSplitShift = 23;
+constexpr int kMergeRowMask = (1 << kMergeSplitShift) - 1;
+static_assert(((int64_t)(kMaxSplits - 1) << kMergeSplitShift) <= 0x7fffffff, "split count bits overflow");
 
 // Kernel-side dtype codes (same values as va_dtype).
 enum : int { kF32 = 0, kF16 = 1, kBF16 = 2, kQ8 = 3 };
@@ -55,7 +61,6 @@ struct PartialParams {
   float* lse;             // direct mode lse (may be NULL)
   float* part_o;          // [S][nrows][D]
   uint64_t* part_ml;      // [S][nrows] (m, l) pairs: m (log2 units) in the low word, l in the high word
-  int32_t* part_n;        // ragged calls: [nrows] splits that hold keys of the row's sequence (written by split 0); else NULL
   const int2* items;      // ragged calls: the work list (sequence, row group << 16 | split << 8 | KV head)
   const int32_t* item_count;  // ragged calls: entries of `items` in use
   uint32_t* flags;
@@ -75,7 +80,6 @@ struct PartialParams {
 struct MergeParams {
   const float* part_o;
   const uint64_t* part_ml;
-  const int32_t* part_n;
   void* out;
   float* lse;
   const int32_t* merge_rows;  // ragged: packed rows to merge, in order; NULL: row = block / heads

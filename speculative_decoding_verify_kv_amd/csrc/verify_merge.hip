@@ -7,10 +7,9 @@
 // merge step of the split-KV schedule on the page "perf(gfx1100): speed up
 // long-context DFlash verify 13.4% with FA2 split-KV and retain HipGraph/Redline
 // PM4" (Performance, batch-16 kernel screen).  In a ragged call only the
-// first n splits of a row hold keys (n, written by the partial kernel's split
-// 0, is below S for a sequence too short to fill S splits of the minimum
-// size); empty splits
-// (l == 0) get weight 0 and their O is never used; a NaN l (a split that saw
+// first n splits of a row hold keys (n, carried in the row's entry of the
+// work list, is below S for a sequence too short to fill S splits of the
+// minimum size); empty splits (l == 0) get weight 0 and their O is never used; a NaN l (a split that saw
 // bad metadata) makes the row NaN.
 //
 // One workgroup of 8 waves per (row, head).  Wave w owns splits w, w + 8,
@@ -99,13 +98,11 @@ __device__ __forceinline__ void load_header(const uint64_t* x, float& m, float& 
 // most one split, and their sums are added in wave order), so the two agree
 // bit for bit.
 template <int D>
-__device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, int lane) {
+__device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, int Sr, int lane) {
   constexpr int E = D / 64;
   constexpr int HJ = kMaxSplits / 64;
   typedef typename VecT<E>::type vec;
   const int S = p.S;
-  const int Sr = max(1, min(S, *reinterpret_cast<const __attribute__((address_space(4))) int*>(
-                                    (uintptr_t)(p.part_n + R))));
   const int64_t kstride = p.nrows * D;
   float mh[HJ], lh[HJ];
 #pragma unroll
@@ -181,30 +178,31 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   // list, one workgroup per (row, head); the rest follow, one wave per
   // (row, head), 8 to a workgroup.
   int64_t R = blockIdx.x;
+  int Sr = p.S;  // splits that hold keys of the row's sequence (fewer for a short one in a ragged call)
   if (p.merge_rows) {
+    // each row entry carries its sequence's split count; the entry a heavy
+    // row would take is loaded beside the counts (it lies inside the list:
+    // the grid is the row capacity times the heads) and used only if it is one
     const auto* mc = reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)p.merge_count);
+    const int64_t kh = R / p.heads;
+    const int eh = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.merge_rows + kh));
     const int64_t heavy = (int64_t)mc[1] * p.heads;
     if (R >= heavy) {
       const int64_t pr = heavy + (R - heavy) * kMergeWaves + (threadIdx.x >> 6);
       if (pr >= (int64_t)mc[0] * p.heads) return;
       const int64_t k = pr / p.heads;
-      const int row = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.merge_rows + k));
-      merge_one_wave<D>(p, (int64_t)row * p.heads + (pr - k * p.heads), threadIdx.x & 63);
+      const int e = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.merge_rows + k));
+      merge_one_wave<D>(p, (int64_t)(e & kMergeRowMask) * p.heads + (pr - k * p.heads),
+                        max(1, min(p.S, (e >> kMergeSplitShift) + 1)), threadIdx.x & 63);
       return;
     }
-    const int64_t k = R / p.heads;
-    const int row = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.merge_rows + k));
-    R = (int64_t)row * p.heads + (R - k * p.heads);
+    R = (int64_t)(eh & kMergeRowMask) * p.heads + (R - kh * p.heads);
+    Sr = max(1, min(p.S, (eh >> kMergeSplitShift) + 1));
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int S = p.S;
-  // splits that hold keys of this row's sequence (ragged calls: a short
-  // sequence fills fewer than S); the later ones hold stale data and are
-  // never weighed
-  const int Sr = !p.part_n ? S
-                           : max(1, min(S, *reinterpret_cast<const __attribute__((address_space(4))) int*>(
-                                               (uintptr_t)(p.part_n + R))));
+  // splits past Sr hold stale data and are never weighed
   const int64_t kstride = p.nrows * D;
 
   auto load = [&](int k) __attribute__((always_inline)) -> vec {

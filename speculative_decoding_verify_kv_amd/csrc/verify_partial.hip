@@ -508,13 +508,6 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   // ---- this split's pages (cut at the group's last visible key) and tiles of 4 pages ----
   const int npages = (ctx + kPage - 1) / kPage;
   const int pps = SQ ? max((npages + p.S - 1) / p.S, kMinSplitPages) : (npages + p.S - 1) / p.S;
-  if constexpr (SQ) {
-    if (split == 0 && !p.direct && tid < QROWS && rowbase + tid < M) {
-      // how many splits hold keys of this sequence, for the merge of each row
-      const int r = rowbase + tid, hl = r / B, b = r - hl * B;
-      p.part_n[(r0 + b) * p.H + kvh * p.G + hl] = max(1, (npages + pps - 1) / pps);
-    }
-  }
   const int p_begin = min(split * pps, npages);
   const int p_end = max(p_begin, min(min(p_begin + pps, npages), vis_pages));
   const int npg = p_end - p_begin;

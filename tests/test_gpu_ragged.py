@@ -366,7 +366,8 @@ def _work_list_model(w, cu, S, plan, ctx_lens=None):
             for g in range(groups):
                 for kvh in range(w.KVH):
                     items.append((word, (g << 16) | (sp << 8) | kvh))
-        merge_rows.extend(range(a, a + rows))
+        # each row entry carries its sequence's split count less one from bit 23
+        merge_rows.extend(r | ((splits - 1) << 23) for r in range(a, a + rows))
         heavy += rows if splits > 8 else 0
     return items, merge_rows, heavy
 
@@ -377,7 +378,7 @@ def _read_work_list(ws, w, plan):
     smax = info.max_splits
     off = 256
     if smax > 1:
-        off = -(-(256 + smax * nrows * (w.D + 2) * 4 + nrows * 4) // 256) * 256
+        off = -(-(256 + smax * nrows * (w.D + 2) * 4) // 256) * 256
     raw = ws.cpu().numpy()
     cnt = raw[off:off + 12].view(np.int32)
     mr_bytes = -(-plan.problem.max_total_rows * 4 // 16) * 16

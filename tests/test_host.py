@@ -64,9 +64,8 @@ def test_headline_plan_and_workspace(lib):
     assert info.num_splits == 64 and info.max_splits == 64
     assert info.pages_per_split == 32
     nrows = 1 * 16 * 24
-    # flag header, then fp32 O, m and l per split and row, then one int32 per
-    # row: how many splits hold keys of the row's sequence
-    assert info.workspace_bytes == 256 + 64 * nrows * (256 + 2) * 4 + nrows * 4
+    # flag header, then fp32 O, m and l per split and row
+    assert info.workspace_bytes == 256 + 64 * nrows * (256 + 2) * 4
     assert p.workspace_bytes == info.workspace_bytes
 
 
@@ -283,11 +282,10 @@ def test_ragged_plan_sizes_by_packed_rows(lib):
     plan = va.verify_attn_plan_for_cus(prob, 8, 256)
     info = plan.info()
     assert info.rows_per_group == 96 and info.row_groups == 7  # 600 rows -> 38 tiles -> 7 groups of 6
-    # header, fp32 partials of 8 splits and one int32 per (row, head), then
-    # (256-byte aligned) the work list: 2 counts in 16 bytes, the 149 packed
+    # header, fp32 partials of 8 splits, then (256-byte aligned) the work list: 2 counts in 16 bytes, the 149 packed
     # rows (padded to 16 bytes) and 8 splits x 14 row groups x 4 KV heads
     # entries of 8 bytes (14 = (149 * 6 + 5 * 95) // 96 groups at most)
-    parts = 256 + 8 * 149 * 24 * 258 * 4 + 149 * 24 * 4
+    parts = 256 + 8 * 149 * 24 * 258 * 4
     assert info.workspace_bytes == -(-parts // 256) * 256 + 16 + 608 + 8 * 14 * 4 * 8
     # the plan's own split count is sized for one long decode sequence (one
     # row group per KV head) filling the CUs that two minimum-size splits per
