@@ -281,6 +281,41 @@ def test_short_sequences_leave_their_extra_splits(S_):
     assert np.abs(lse.cpu().double().numpy()[:n] - lref).max() <= 2e-3
 
 
+def test_largest_split_count_in_row_entries():
+    """At S = 256 a 131,072-token sequence fills every split (32 pages each),
+    so its rows' entries in the merge's list carry 255 (splits - 1) in bits
+    23-30; a 600-token sequence beside it fills two (38 pages).  The partial area
+    is filled with NaN bytes first, so a split read past a row's own count
+    would show.  The list read back equals its rule, and the outputs match
+    the oracle."""
+    import torch
+
+    w = S.make_workload("split256", ctx_lens=[131072, 600], rows=[3, 2], H=8, KVH=2, D=64, q_dtype="bf16",
+                        kv_dtype="q8_0", seed=71, permute=True, spare_pages=3, poison=True)
+    say(f"[case] split counts at S=256 ctx={w.ctx_lens.tolist()} rows={np.diff(w.cu_rows).tolist()}")
+    ref, lref = oracle.attention(w)
+    dev = vdev.to_device(w)
+    plan = va.verify_attn_plan(vdev.problem_for(w, out_dtype="f32"), 256, 0)
+    ws = vdev.workspace(plan)
+    ws[256:] = 0xFF
+    cap = plan.problem.max_total_rows
+    out = torch.full((cap, w.H, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((cap, w.H), float("nan"), dtype=torch.float32, device="cuda")
+    va.verify_attn_run_ragged(plan, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_scale"], dev["v_scale"],
+                              dev["block_table"], dev["ctx_lens"], dev["cu_rows"], dev["parent"], 256, out, lse, ws)
+    torch.cuda.synchronize()
+    assert va.verify_attn_read_flags(plan, ws) == 0
+    n_items, n_rows, n_heavy, it, mrows = _read_work_list(ws, w, plan)
+    want_items, want_rows, want_heavy = _work_list_model(w, w.cu_rows, 256, plan)
+    assert (mrows >> 23).tolist() == [255, 255, 255, 1, 1]
+    assert n_items == len(want_items) and n_rows == len(want_rows) and n_heavy == want_heavy == 3
+    assert mrows.tolist() == want_rows
+    assert [tuple(x) for x in it.tolist()] == want_items
+    n = w.total_rows
+    check_parity(out.cpu().double().numpy()[:n], ref, "f32", "split counts at S=256")
+    assert np.abs(lse.cpu().double().numpy()[:n] - lref).max() <= 2e-3
+
+
 @pytest.mark.parametrize("kv,S_", [("q8_0", 0), ("f16", 3)])
 @pytest.mark.parametrize("nseq", [150, 64, 65])
 def test_many_sequences(kv, S_, nseq):
