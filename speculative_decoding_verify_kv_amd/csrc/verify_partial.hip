@@ -393,8 +393,9 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   if constexpr (SQ) {
     // Splits of a sequence take at least kMinSplitPages pages each, so a
     // short sequence fills fewer than S of them.  A workgroup past those has
-    // no keys: it leaves before copying anything (split 0 records the count
-    // for the merge).  ctx is already waited for here, ahead of the Q copies.
+    // no keys: it leaves before copying anything (the merge reads only the
+    // splits that hold keys; each row's entry in its list carries the count).
+    // ctx is already waited for here, ahead of the Q copies.
     const bool ctx_bad = ctx < B || ctx > p.max_ctx || ctx > p.max_pages * kPage;
     const int np = ctx_bad ? 0 : (ctx + kPage - 1) / kPage;
     const int pp = max((np + p.S - 1) / p.S, kMinSplitPages);
