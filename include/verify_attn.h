@@ -73,9 +73,10 @@
  * WORKSPACE
  *   verify_attn_plan reports workspace_bytes.  The first 256 bytes hold a
  *   uint32 flag word (kernels OR error bits into it); then the fp32 split
- *   partials; a ragged plan's workspace ends with the call's work list (what verify_attn_run_ragged's first kernel
- *   writes for the other two).  Zero the workspace once after allocating it;
- *   the flags stay set until verify_attn_read_flags clears them.
+ *   partials; a ragged plan's workspace ends with the call's work list
+ *   (what verify_attn_run_ragged's first kernel writes for the other two).
+ *   Zero the workspace once after allocating it; the flags stay set until
+ *   verify_attn_read_flags clears them.
  *
  * ERRORS (fail closed: nothing is launched on any error; page "perf(gfx1100):
  * speed up long-context DFlash verify 13.4% with FA2 split-KV and retain
