@@ -23,7 +23,7 @@ from .test_gpu_ragged import run_ragged
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 @pytest.fixture(scope="module", autouse=True)
