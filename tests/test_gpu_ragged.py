@@ -466,7 +466,7 @@ def test_work_list_matches_its_rule(name):
         assert [tuple(x) for x in it.tolist()] == want_items
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_work_list_random_batches(seed):
     """Random batches (1 to 150 sequences, 0 to 9 rows, contexts up to 3,000,
     the plan's S or a random one), some with bad cu_rows entries or contexts:
