@@ -168,3 +168,42 @@ def test_promote_one_and_three_launch_forms(nseq):
     assert _same_pools(dev, w.k_pool, w.v_pool, w.k_scale, w.v_scale)
     status = int(wss[0][4:8].cpu().numpy().view(np.uint32)[0])
     assert status == (0 if one else int(va.VA_FLAG_BAD_PATH))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_promote_random(seed):
+    """Seeded random batches: head_dim 64/128/256, 8-bit or fp16 KV, 4 head
+    layouts, B 2-32 rows of direct chain plus draft tree, 1-29 sequences (so
+    both the one-launch form, up to 256 (sequence, slot) pairs, and the
+    three-launch form run), and per sequence an empty path or the path from
+    a random ancestor down to a random row.  Pools bit for bit and new_ctx
+    against the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    H, KVH = [(4, 2), (8, 1), (24, 4), (6, 6)][int(rng.integers(0, 4))]
+    kv = str(rng.choice(["q8_0", "f16"]))
+    B = int(rng.integers(2, 33))
+    nseq = int(rng.integers(1, 30))
+    n_direct = int(rng.integers(0, B))
+    ctxs = [int(rng.integers(B, 3000)) for _ in range(nseq)]
+    par = np.stack([S.tree_parent(n_direct, B - n_direct, rng) for _ in range(nseq)])
+    w = S.make_workload(f"promote_rand{seed}", ctx_lens=ctxs, B=B, H=H, KVH=KVH, D=D, q_dtype="bf16",
+                        kv_dtype=kv, seed=7000 + seed, permute=True, spare_pages=3, poison=True, parent=par)
+    acc = np.zeros((nseq, B), np.int32)
+    n = np.zeros(nseq, np.int32)
+    for s in range(nseq):
+        if rng.random() < 0.15:
+            continue
+        chain = [int(rng.integers(0, B))]
+        while par[s][chain[-1]] >= 0:
+            chain.append(int(par[s][chain[-1]]))
+        pth = chain[::-1][int(rng.integers(0, len(chain))):]
+        acc[s, :len(pth)] = pth
+        n[s] = len(pth)
+    say(f"[case] promote random seed={seed} D={D} H={H}/{KVH} kv={kv} B={B} nseq={nseq} pairs={nseq * B} "
+        f"n={n.tolist()}")
+    k, v, ks, vs, new_ctx = oracle.promote_kv(w, acc, n)
+    dev, got_ctx, flags = gpu_promote(w, acc, n)
+    assert flags == 0
+    assert np.array_equal(got_ctx, new_ctx)
+    assert _same_pools(dev, k, v, ks, vs)
