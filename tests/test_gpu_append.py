@@ -71,6 +71,35 @@ def test_append_bitwise(kv_dtype, new_dtype, D):
         assert np.array_equal(_bytes(dev["v_scale"]), rvs.view(np.uint8).reshape(-1))
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_append_random_bitwise(seed):
+    """Seeded random batches: head_dim 64/128/256, 8-bit or fp16 pools, 4
+    head layouts, B 1-32, 1-20 sequences with contexts from B to 3,000 (the
+    drafted slots often straddle a page), f32 / f16 / bf16 rows.  Pools and
+    scales bit for bit against the oracle's append, untouched slots
+    included."""
+    rng = np.random.default_rng(8000 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    H, KVH = [(4, 2), (8, 1), (24, 4), (6, 6)][int(rng.integers(0, 4))]
+    kv = str(rng.choice(["q8_0", "f16"]))
+    new_dtype = str(rng.choice(["f32", "f16", "bf16"]))
+    B = int(rng.integers(1, 33))
+    nseq = int(rng.integers(1, 21))
+    ctxs = [int(rng.integers(B, 3001)) for _ in range(nseq)]
+    w = S.make_workload(f"append_rand{seed}", ctx_lens=ctxs, B=B, H=H, KVH=KVH, D=D, q_dtype="bf16", kv_dtype=kv,
+                        seed=8000 + seed, permute=True, spare_pages=4, poison=True)
+    say(f"[case] append random seed={seed} D={D} H={H}/{KVH} kv={kv} new={new_dtype} B={B} nseq={nseq}")
+    k_new, v_new = S.new_kv_rows(w, new_dtype, seed=seed)
+    rk, rv, rks, rvs = oracle.append_kv(w, k_new, v_new, new_dtype)
+    dev, flags = gpu_append(w, k_new, v_new, new_dtype)
+    assert flags == 0
+    assert np.array_equal(_bytes(dev["k_pool"]), rk.view(np.uint8).reshape(-1))
+    assert np.array_equal(_bytes(dev["v_pool"]), rv.view(np.uint8).reshape(-1))
+    if kv == "q8_0":
+        assert np.array_equal(_bytes(dev["k_scale"]), rks.view(np.uint8).reshape(-1))
+        assert np.array_equal(_bytes(dev["v_scale"]), rvs.view(np.uint8).reshape(-1))
+
+
 def test_append_extreme_blocks_bitwise():
     """Zero blocks, tiny and huge magnitudes, exact ties and NaN entries."""
     say("[case] append extreme blocks")
