@@ -290,6 +290,11 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   constexpr int QROWS = 16 * NT;
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
+  // The kernel arguments span four 64-byte scalar-cache lines.  Reading one
+  // field of each here puts all four in the first round trip; the compiler
+  // would otherwise fetch them in dependent batches as branches need them,
+  // a memory latency each when every workgroup starts at once.
+  asm volatile("" ::"s"(p.q), "s"(p.cu_rows), "s"(p.S), "s"(p.scale_log2));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -361,7 +366,13 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   // (3) the group's Q rows as raw 16-byte units; (4) the parent array.
   // Uniform metadata is read through the scalar cache (it is never written
   // while the kernel runs), so no vector wait sits in front of the loads below.
-  int ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s));
+  // Scalar loads return out of order, so a use of any of them waits for all:
+  // in uniform calls ctx and the page ids are read after the Q copies are
+  // issued, which then need not wait for those memory round trips.  (Ragged
+  // calls read ctx first: a workgroup past its sequence's splits leaves
+  // before copying anything.)
+  int ctx = 0;
+  if constexpr (SQ) ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s));
   const int npg_max = (p.max_ctx + kPage - 1) / kPage;
   const int pps_spec = SQ ? max((npg_max + p.S - 1) / p.S, kMinSplitPages) : (npg_max + p.S - 1) / p.S;
   const int pb_spec = min(split * pps_spec, npg_max);
@@ -383,13 +394,16 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   // K tiles right away; the page ids of those tiles (split page 4j + q) come
   // through the scalar cache.  fp32 Q is loaded below by all threads.
   int kid[L::RK - 1];
+  auto load_kid = [&](int z) __attribute__((always_inline)) {
 #pragma unroll
-  for (int j = 0; j < L::RK - 1; ++j) {
-    const int off = pb_spec + 4 * j + (wave - kRoleWaves);
-    kid[j] = 0;
-    if (!is_score && off < pe_spec)
-      kid[j] = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(bt_row + off));
-  }
+    for (int j = 0; j < L::RK - 1; ++j) {
+      const int off = pb_spec + 4 * j + (wave - kRoleWaves);
+      kid[j] = 0;
+      if (!is_score && off < pe_spec)
+        kid[j] = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(bt_row + off + z));
+    }
+  };
+  if constexpr (SQ) load_kid(0);
   if constexpr (SQ) {
     // Splits of a sequence take at least kMinSplitPages pages each, so a
     // short sequence fills fewer than S of them.  A workgroup past those has
@@ -435,6 +449,14 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
     }
   }
 
+  if constexpr (!SQ) {
+    // z is 0; taking it from an asm statement placed after the Q copies keeps
+    // the compiler from moving these loads (of invariant memory) ahead of them
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s + z));
+    load_kid(z);
+  }
   const int upr = qf32 ? D / 4 : D / 8;  // 16-byte Q units per row (a power of two)
   constexpr int QU_MAX = (QROWS * (D / 4) + kBlockThreads - 1) / kBlockThreads;
   u32x4 qraw[QU_MAX];
