@@ -26,8 +26,11 @@ SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip", "ragged_schedule
 # Its instructions are scheduled for instruction-level parallelism rather
 # than occupancy (the kernel runs one workgroup per CU whatever the
 # schedule): 0.2-0.4 us less per launch, the same registers and results.
+# Its first seven kernel arguments (what a workgroup needs to issue its Q
+# copies) are preloaded into SGPRs at wave launch.
 PER_SOURCE_FLAGS = {"verify_partial.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
-                                           "-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+                                           "-mllvm", "-amdgpu-sched-strategy=max-ilp",
+                                           "-mllvm", "-amdgpu-kernarg-preload-count=7"]}
 ARCH = "gfx950"
 
 

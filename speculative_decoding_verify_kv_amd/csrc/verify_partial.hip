@@ -291,10 +291,13 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) char*)smem);
 
   // The kernel arguments span four 64-byte scalar-cache lines.  Reading one
-  // field of each here puts all four in the first round trip; the compiler
+  // field of each at once puts all four in one round trip; the compiler
   // would otherwise fetch them in dependent batches as branches need them,
-  // a memory latency each when every workgroup starts at once.
-  asm volatile("" ::"s"(p.q), "s"(p.cu_rows), "s"(p.S), "s"(p.scale_log2));
+  // a memory latency each when every workgroup starts at once.  Uniform
+  // calls get the arguments their Q copies need in SGPRs at wave launch (the
+  // leading kernel arguments, preloaded) and touch the lines after issuing
+  // the copies, below.
+  if constexpr (SQ) asm volatile("" ::"s"(p.q), "s"(p.cu_rows), "s"(p.num_seqs), "s"(p.S));
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,7 +345,7 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   int B = p.B;
   int64_t r0 = (int64_t)s * p.B;
   bool bad_rows = false;
-  if (p.cu_rows) {
+  if (SQ && p.cu_rows) {
     const auto* cu = reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.cu_rows + s));
     const int a = cu[0], e = cu[1];
     bad_rows = a < 0 || e < a || e > p.total_rows || e - a > p.B;
@@ -358,7 +361,23 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
     return;
   }
 
-  const int32_t* bt_row = p.block_table + (int64_t)s * p.max_pages;
+  const int32_t* bt_row;
+  int npg_max, pps_spec, pb_spec, pe_spec;
+  // The split's place at ctx = max_ctx and its row of the block table (z is
+  // 0: in uniform calls it comes from an asm statement after the Q copies,
+  // which keeps these reads of the argument block behind them).
+  auto split_meta = [&](int z) __attribute__((always_inline)) {
+    bt_row = p.block_table + (int64_t)s * p.max_pages + z;
+    npg_max = (p.max_ctx + z + kPage - 1) / kPage;
+    pps_spec = SQ ? max((npg_max + p.S - 1) / p.S, kMinSplitPages) : (npg_max + p.S - 1) / p.S;
+    pb_spec = min(split * pps_spec, npg_max);
+    pe_spec = min(pb_spec + pps_spec, npg_max);
+  };
+  int id_spec = 0;
+  if constexpr (SQ) {
+    split_meta(0);
+    if (tid < 128 && pb_spec + tid < pe_spec) id_spec = bt_row[pb_spec + tid];
+  }
 
   // ---- prologue loads, all in flight together ----
   // (1) ctx; (2) the block-table entries of this split as placed for
@@ -373,12 +392,6 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   // before copying anything.)
   int ctx = 0;
   if constexpr (SQ) ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s));
-  const int npg_max = (p.max_ctx + kPage - 1) / kPage;
-  const int pps_spec = SQ ? max((npg_max + p.S - 1) / p.S, kMinSplitPages) : (npg_max + p.S - 1) / p.S;
-  const int pb_spec = min(split * pps_spec, npg_max);
-  const int pe_spec = min(pb_spec + pps_spec, npg_max);
-  int id_spec = 0;
-  if (tid < 128 && pb_spec + tid < pe_spec) id_spec = bt_row[pb_spec + tid];
 
   const bool qf32 = p.q_dtype == kF32;
   h16* q_lds = reinterpret_cast<h16*>(smem + L::QST_OFF);
@@ -451,11 +464,15 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
 
   if constexpr (!SQ) {
     // z is 0; taking it from an asm statement placed after the Q copies keeps
-    // the compiler from moving these loads (of invariant memory) ahead of them
+    // the compiler from moving these loads (of invariant memory) ahead of
+    // them.  Its inputs, one field of each line of the argument block that
+    // is not preloaded, bring those lines in one round trip.
     int z;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z) : "s"(p.k_pool), "s"(p.cu_rows), "s"(p.num_seqs), "s"(p.scale_log2));
+    split_meta(z);
     ctx = *reinterpret_cast<const __attribute__((address_space(4))) int*>((uintptr_t)(p.ctx_lens + s + z));
-    load_kid(z);
+    load_kid(0);
+    if (tid < 128 && pb_spec + tid < pe_spec) id_spec = bt_row[pb_spec + tid];
   }
   const int upr = qf32 ? D / 4 : D / 8;  // 16-byte Q units per row (a power of two)
   constexpr int QU_MAX = (QROWS * (D / 4) + kBlockThreads - 1) / kBlockThreads;
@@ -1168,7 +1185,25 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
 // for the group's distinct rows, the same in either body), so the choice
 // changes no value.
 template <int D, int KVT, int NT, bool SQ>
-__global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const PartialParams p) {
+//
+// The leading arguments repeat the fields of the parameter block that a
+// workgroup of a uniform call needs to issue its Q copies; the build preloads
+// them into SGPRs at wave launch (-amdgpu-kernarg-preload-count), so the
+// copies wait for no read of the argument block.  (A ragged call's first
+// reads are the work list and cu_rows, which need the block anyway.)
+__global__ __launch_bounds__(kBlockThreads, 1) void verify_partial_kernel(const void* q, int32_t B, int32_t H, int32_t G,
+                                                                           int32_t S, int32_t row_groups, int32_t q_dtype,
+                                                                           const PartialParams p0) {
+  PartialParams p = p0;
+  if constexpr (!SQ) {
+    p.q = q;
+    p.B = B;
+    p.H = H;
+    p.G = G;
+    p.S = S;
+    p.row_groups = row_groups;
+    p.q_dtype = q_dtype;
+  }
   constexpr bool kThinBody = SQ && NT > 2;
   constexpr int kBytes = kThinBody && Lay<D, KVT, 2>::BYTES > Lay<D, KVT, NT>::BYTES ? Lay<D, KVT, 2>::BYTES
                                                                                      : Lay<D, KVT, NT>::BYTES;
@@ -1212,10 +1247,11 @@ static hipError_t launch_t(const PartialParams& p, hipStream_t stream) {
   if (p.items) {
     // ragged: one workgroup per entry the work list can hold
     hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, true>), dim3((unsigned)p.item_cap),
-                       dim3(kBlockThreads), 0, stream, p);
+                       dim3(kBlockThreads), 0, stream, p.q, p.B, p.H, p.G, p.S, p.row_groups, p.q_dtype, p);
   }
   else
-    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, false>), grid, dim3(kBlockThreads), 0, stream, p);
+    hipLaunchKernelGGL((verify_partial_kernel<D, KVT, NT, false>), grid, dim3(kBlockThreads), 0, stream, p.q, p.B, p.H,
+                       p.G, p.S, p.row_groups, p.q_dtype, p);
   return hipGetLastError();
 }
 
