@@ -30,7 +30,8 @@ SOURCES = ["api.hip", "verify_partial.hip", "verify_merge.hip", "ragged_schedule
 # copies) are preloaded into SGPRs at wave launch.
 PER_SOURCE_FLAGS = {"verify_partial.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
                                            "-mllvm", "-amdgpu-sched-strategy=max-ilp",
-                                           "-mllvm", "-amdgpu-kernarg-preload-count=7"]}
+                                           "-mllvm", "-amdgpu-kernarg-preload-count=7"],
+                    "verify_merge.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=5"]}
 ARCH = "gfx950"
 
 

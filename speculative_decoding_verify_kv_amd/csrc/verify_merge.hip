@@ -165,8 +165,9 @@ __device__ __forceinline__ void merge_one_wave(const MergeParams& p, int64_t R, 
   store_row<E>(p, R, lane, acc, inv, nan_row, M, L);
 }
 
-template <int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const MergeParams p) {
+// RAGGED: the rows come from the work list (merge_rows, merge_count).
+template <int D, bool RAGGED>
+__device__ __forceinline__ void merge_body(const MergeParams& p) {
   constexpr int E = D / 64;  // outputs per lane
   constexpr int HJ = kMaxSplits / 64;
   typedef typename VecT<E>::type vec;
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   // (row, head), 8 to a workgroup.
   int64_t R = blockIdx.x;
   int Sr = p.S;  // splits that hold keys of the row's sequence (fewer for a short one in a ragged call)
-  if (p.merge_rows) {
+  if constexpr (RAGGED) {
     // each row entry carries its sequence's split count; the entry a heavy
     // row would take is loaded beside the counts (it lies inside the list:
     // the grid is the row capacity times the heads) and used only if it is one
@@ -287,16 +288,51 @@ __global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const Me
   store_row<E>(p, R, lane, sum, inv, nan_row, M, L);
 }
 
+// Uniform calls: the leading arguments repeat the fields of the parameter
+// block that the first loads need (the partials' addresses, the split count,
+// the heads); the build preloads them into SGPRs at wave launch
+// (-amdgpu-kernarg-preload-count), so the header and partial loads wait for
+// no read of the argument block.
+template <int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_kernel(const float* part_o, const uint64_t* part_ml,
+                                                                      int64_t nrows, int32_t S, int32_t heads,
+                                                                      const MergeParams p0) {
+  MergeParams p = p0;
+  p.part_o = part_o;
+  p.part_ml = part_ml;
+  p.nrows = nrows;
+  p.S = S;
+  p.heads = heads;
+  merge_body<D, false>(p);
+}
+
+// Ragged calls read the work list first, which needs the parameter block
+// anyway: no preloaded arguments, which would only add to the launch.
+template <int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void verify_merge_ragged_kernel(const MergeParams p) {
+  merge_body<D, true>(p);
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.nrows);
+  const dim3 block(64 * kMergeWaves);
+#define VA_MERGE_LAUNCH(DD)                                                                                       \
+  do {                                                                                                             \
+    if (p.merge_rows)                                                                                              \
+      hipLaunchKernelGGL((verify_merge_ragged_kernel<DD>), grid, block, 0, stream, p);                             \
+    else                                                                                                           \
+      hipLaunchKernelGGL((verify_merge_kernel<DD>), grid, block, 0, stream, p.part_o, p.part_ml, p.nrows, p.S,     \
+                         p.heads, p);                                                                              \
+  } while (0)
   switch (p.D) {
-    case 256: hipLaunchKernelGGL(verify_merge_kernel<256>, grid, dim3(64 * kMergeWaves), 0, stream, p); break;
-    case 128: hipLaunchKernelGGL(verify_merge_kernel<128>, grid, dim3(64 * kMergeWaves), 0, stream, p); break;
-    case 64: hipLaunchKernelGGL(verify_merge_kernel<64>, grid, dim3(64 * kMergeWaves), 0, stream, p); break;
+    case 256: VA_MERGE_LAUNCH(256); break;
+    case 128: VA_MERGE_LAUNCH(128); break;
+    case 64: VA_MERGE_LAUNCH(64); break;
     default: return hipErrorInvalidValue;
   }
+#undef VA_MERGE_LAUNCH
   return hipGetLastError();
 }
 
