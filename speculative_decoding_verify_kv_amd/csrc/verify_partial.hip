@@ -401,11 +401,12 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
   constexpr int QSW = (D / 8 >= 16) ? 15 : 7;
   auto q_unit = [&](int rr, int u) __attribute__((always_inline)) { return q_lds + rr * D + 8 * (u ^ (rr & QSW)); };
 
-  // 16-bit Q: the output waves copy the group's Q rows into the staging area
-  // with LDS-DMA (slot s of the swizzled layout = its own 16-byte source
-  // unit), so they hold no vector load of their own and can send the first
-  // K tiles right away; the page ids of those tiles (split page 4j + q) come
-  // through the scalar cache.  fp32 Q is loaded below by all threads.
+  // 16-bit Q: the waves copy the group's Q rows into the staging area with
+  // LDS-DMA (slot s of the swizzled layout = its own 16-byte source unit),
+  // so the output waves hold no vector load of their own and can send the
+  // first K tiles right away; the page ids of those tiles (split page
+  // 4j + q) come through the scalar cache.  fp32 Q is loaded below by all
+  // threads.
   int kid[L::RK - 1];
   auto load_kid = [&](int z) __attribute__((always_inline)) {
 #pragma unroll
@@ -432,11 +433,14 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
     }
   }
   constexpr int QUPR = D / 8;                          // 16-byte units of a 16-bit Q row
-  constexpr int QSPW = QROWS * QUPR / kRoleWaves;      // staging units per output wave
-  constexpr int QDMA = QSPW / 64;                      // LDS-DMA instructions per output wave
+  // All 8 waves copy Q when the rows split into whole instructions per wave
+  // (half the copy instructions per wave: the copies are issued sooner)
+  constexpr bool Q8W = (QROWS * QUPR / 8) % 64 == 0;
+  constexpr int QSPW = QROWS * QUPR / (Q8W ? 8 : kRoleWaves);  // staging units per copying wave
+  constexpr int QDMA = QSPW / 64;                      // LDS-DMA instructions per copying wave
   static_assert(QSPW % 64 == 0, "whole Q DMA instructions");
-  if (!is_score && !qf32) {
-    const int q4 = wave - kRoleWaves;
+  if (!qf32 && (Q8W || !is_score)) {
+    const int q4 = Q8W ? wave : wave - kRoleWaves;
     constexpr int RPI = 64 / QUPR;  // staged rows per instruction
     int rr = (q4 * QSPW + lane) / QUPR;
     const int phys = lane & (QUPR - 1);
@@ -699,6 +703,8 @@ __device__ __forceinline__ void partial_body(const PartialParams p, char* smem) 
     } else {
       wait_vmcnt<0>();
     }
+  } else if (Q8W) {
+    wait_vmcnt<0>();  // this score wave's Q copies
   }
   __syncthreads();
   if (!qf32) {
